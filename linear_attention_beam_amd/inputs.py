@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs for the large-beam Gated DeltaNet decode step.
+
+This module draws random numbers and encodes them; it holds none of the decode arithmetic.  The
+oracle (under ``oracle/``) and the HIP path both take their inputs from here and from nowhere else.
+
+The pages publish no workload: the review of OneLA ("Scientific Impact Assessment: OneLA", §2
+Methodological Rigor and §5 Strengths & Limitations) says the industrial traffic and the 405 operator
+shapes are not released.  The five configurations below stand in for that sweep.  They keep its axes
+(request count, beam width, decode length, recurrent geometry) and the structure the abstract names
+(hundreds of beams that share one prompt-derived state and diverge over a few decode steps).
+
+Recipe (every configuration):
+  * q, k ~ N(0, 1) drawn in float32, divided by their float32 L2 norm, then rounded once to the
+    decode dtype (bfloat16 round-to-nearest-even for the bf16 configurations).  Never renormalised.
+  * v ~ N(0, 1) float32, rounded to the decode dtype.
+  * alpha ~ U(alpha_lo, 1), beta ~ U(0, 1), float32.
+  * parents: step 1 has a single pseudo-parent (index 0, the shared state).  Later steps draw each
+    new beam's parent independently: uniformly over the previous beams, or from a Zipf law truncated to
+    ranks 1..B_prev (P(rank) proportional to rank^-s, parent = rank - 1, beam index = score rank).
+  * S_ctx: either N(0, std^2) directly, or the inputs of a prefill of N GDN steps from the zero state
+    with the same k/v/alpha/beta distributions (float32, not rounded).  Turning those prefill inputs
+    into S_ctx is GDN arithmetic and is done by the caller (the oracle's prefill or the GPU prefill).
+  * Streams: numpy PCG64 seeded by SeedSequence([0x0E1A, config index, stream, seed]); stream 0 draws
+    S_ctx or the prefill inputs, stream 1 the per-step decode inputs, stream 2 the parents.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+__all__ = [
+    "Config", "CONFIGS", "config", "StepInputs", "PrefillInputs",
+    "decode_inputs", "prefill_inputs", "direct_sctx", "parents_for_step",
+    "f32_to_bf16_bits", "bf16_bits_to_f32",
+]
+
+_SEED_TAG = 0x0E1A
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """One synthetic workload: R requests x H heads x B beams, L decode steps, state d_v x d_k."""
+
+    index: int
+    name: str
+    R: int
+    H: int
+    d_k: int
+    d_v: int
+    B: int
+    L: int
+    qkv_dtype: str          # "f32" or "bf16"
+    alpha_lo: float         # alpha ~ U(alpha_lo, 1)
+    prefill_steps: int      # 0: S_ctx drawn directly with sctx_std
+    sctx_std: float
+    parent_law: str         # "uniform" or "zipf"
+    zipf_s: float
+
+    @property
+    def beam_tokens(self) -> int:
+        """Beam-tokens in one full decode: one beam advanced one step through all H heads."""
+        return self.R * self.B * self.L
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.qkv_dtype == "f32" else 2
+
+
+CONFIGS = [
+    Config(0, "tiny: R=1 H=1 d=16 B=8 L=3 fp32", 1, 1, 16, 16, 8, 3, "f32", 0.9, 0, 0.1, "uniform", 0.0),
+    Config(1, "R=1 H=16 d=128 B=128 L=4 bf16 prefill1024 zipf1.1", 1, 16, 128, 128, 128, 4, "bf16", 0.9,
+           1024, 0.0, "zipf", 1.1),
+    Config(2, "R=8 H=16 d=128 B=256 L=4 bf16 prefill1024 zipf1.1", 8, 16, 128, 128, 256, 4, "bf16", 0.9,
+           1024, 0.0, "zipf", 1.1),
+    Config(3, "R=32 H=16 d=128 B=512 L=8 bf16 prefill5120 zipf1.5", 32, 16, 128, 128, 512, 8, "bf16", 0.9,
+           5120, 0.0, "zipf", 1.5),
+    Config(4, "R=16 H=32 dk=128 dv=256 B=512 L=6 bf16 prefill5120 zipf1.1", 16, 32, 128, 256, 512, 6,
+           "bf16", 0.95, 5120, 0.0, "zipf", 1.1),
+]
+
+
+def config(index: int, **overrides) -> Config:
+    """Return configuration ``index``, optionally with fields replaced (for scaled-down test cases)."""
+    return dataclasses.replace(CONFIGS[index], **overrides) if overrides else CONFIGS[index]
+
+
+# ----------------------------------------------------------------------------------------------
+# bfloat16 encoding (numpy has no bf16 type: values travel as their 16-bit patterns)
+# ----------------------------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); return the uint16 bit patterns."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    rounded = bits + np.uint32(0x7FFF) + lsb
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bfloat16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(cfg: Config, stream: int, seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([_SEED_TAG, cfg.index, stream, seed])))
+
+
+def _unit_rows_f32(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    norm = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))
+    x /= norm[..., None]
+    return x
+
+
+# ----------------------------------------------------------------------------------------------
+# Decode-step inputs
+# ----------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class StepInputs:
+    """Inputs of one decode step.  q, k: [R, B, H, d_k]; v: [R, B, H, d_v]; alpha, beta: [R, B, H];
+    parent: [R, B] int32.  For bf16 configurations ``q``/``k``/``v`` hold uint16 bit patterns."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray
+    beta: np.ndarray
+    parent: np.ndarray
+    dtype: str
+
+    def as_f32(self, name: str) -> np.ndarray:
+        """The exact float32 values of q, k or v."""
+        a = getattr(self, name)
+        return bf16_bits_to_f32(a) if self.dtype == "bf16" else a
+
+
+def parents_for_step(cfg: Config, rng: np.random.Generator, t: int, b_prev: int, n: int) -> np.ndarray:
+    """Parents of the n new beams of step t (1-based) for every request: [R, n] int32 in [0, b_prev)."""
+    if t == 1 or b_prev == 1:
+        return np.zeros((cfg.R, n), dtype=np.int32)
+    if cfg.parent_law == "uniform":
+        return rng.integers(0, b_prev, size=(cfg.R, n), dtype=np.int64).astype(np.int32)
+    ranks = np.arange(1, b_prev + 1, dtype=np.float64)
+    w = ranks ** (-cfg.zipf_s)
+    cdf = np.cumsum(w) / w.sum()
+    cdf[-1] = 1.0
+    u = rng.random((cfg.R, n))
+    idx = np.searchsorted(cdf, u, side="right")
+    return np.minimum(idx, b_prev - 1).astype(np.int32)
+
+
+def decode_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None) -> List[StepInputs]:
+    """All decode-step inputs of one configuration (``steps`` defaults to cfg.L)."""
+    steps = cfg.L if steps is None else steps
+    rng = _rng(cfg, 1, seed)
+    prng = _rng(cfg, 2, seed)
+    R, B, H = cfg.R, cfg.B, cfg.H
+    out = []
+    b_prev = 1
+    for t in range(1, steps + 1):
+        q = _unit_rows_f32(rng, (R, B, H, cfg.d_k))
+        k = _unit_rows_f32(rng, (R, B, H, cfg.d_k))
+        v = rng.standard_normal((R, B, H, cfg.d_v), dtype=np.float32)
+        alpha = rng.uniform(cfg.alpha_lo, 1.0, size=(R, B, H)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, size=(R, B, H)).astype(np.float32)
+        parent = parents_for_step(cfg, prng, t, b_prev, B)
+        if cfg.qkv_dtype == "bf16":
+            q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+        out.append(StepInputs(q, k, v, alpha, beta, parent, cfg.qkv_dtype))
+        b_prev = B
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Shared post-prefill state
+# ----------------------------------------------------------------------------------------------
+
+def direct_sctx(cfg: Config, seed: int = 0) -> np.ndarray:
+    """S_ctx drawn directly as N(0, std^2) float32, [R, H, d_v, d_k] (configurations without prefill)."""
+    rng = _rng(cfg, 0, seed)
+    return (rng.standard_normal((cfg.R, cfg.H, cfg.d_v, cfg.d_k), dtype=np.float32)
+            * np.float32(cfg.sctx_std))
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    """Inputs of the prompt prefill: k [R, N, H, d_k], v [R, N, H, d_v], alpha/beta [R, N, H], float32."""
+
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray
+    beta: np.ndarray
+
+
+def prefill_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None) -> PrefillInputs:
+    """Random prompt of ``steps`` (default cfg.prefill_steps) GDN steps for every request and head."""
+    n = cfg.prefill_steps if steps is None else steps
+    rng = _rng(cfg, 0, seed)
+    R, H = cfg.R, cfg.H
+    k = _unit_rows_f32(rng, (R, n, H, cfg.d_k))
+    v = rng.standard_normal((R, n, H, cfg.d_v), dtype=np.float32)
+    alpha = rng.uniform(cfg.alpha_lo, 1.0, size=(R, n, H)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, size=(R, n, H)).astype(np.float32)
+    return PrefillInputs(k, v, alpha, beta)
