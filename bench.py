@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the large-beam Gated DeltaNet decode step on one MI355X.
+
+One bench "step" is one whole decode of the workload: L onela_step calls (ancestry index update, shared
+S_ctx contraction, key and query replay, record append, output: one fused kernel per call) over
+R requests x B beams x H heads, after onela_reset.  Inputs (all L steps) and the context are resident in
+HBM before timing starts.  value = beam-tokens per second = R * B * L / seconds per decode.
+
+Prints one JSON line.  Extra objects:
+  roofline      the fused step kernel: algorithmic HBM bytes per launch (compulsory traffic, counted from
+                the run's own chain tables) / its average launch time from HIP events in the timed region
+  cpu_baseline  the float64 CPU oracle (record-replay form) timed on whole requests of the same workload
+  fullstate     the controlled FullState path (dense per-beam state) on the same inputs
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.json")
+FUSED_SRC = os.path.join(ROOT, "linear_attention_beam_amd", "csrc", "step_fused.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(FUSED_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(cfg, chains, parents):
+    """Compulsory HBM bytes of each decode step's fused launch.
+
+    chains: [L, R, B, L] int32 tables read back from the run; parents: per-step [R, B] int32.
+    Per step: S_ctx (bf16 high + low halves), q/k/v, alpha/beta, parents, the chain rows read (distinct
+    parents) and written, o (float32), the appended records, and the distinct ancestor records read.
+    """
+    R, H, dk, dv, B, L = cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L
+    s_in = cfg.in_bytes
+    rec = dk * s_in + 4 * dv + 4
+    out = []
+    for t in range(1, L + 1):
+        nbytes = R * H * dv * dk * 4                      # S_ctx hi + lo
+        nbytes += R * B * H * (2 * dk + dv) * s_in        # q, k, v
+        nbytes += R * B * H * 8 + R * B * 4               # alpha, beta, parents
+        nbytes += R * B * H * dv * 4                      # o
+        nbytes += R * B * H * rec                         # records appended
+        nbytes += R * B * L * 4                           # chain table written
+        anc = 0
+        if t > 1:
+            prev = chains[t - 2]
+            for r in range(R):
+                ps = np.unique(parents[t - 1][r])
+                rows = prev[r, ps, : t - 1]
+                anc += np.unique(rows).size
+                nbytes += ps.size * (t - 1) * 4           # chain rows read
+        nbytes += anc * H * rec                           # distinct ancestor records read
+        out.append(nbytes)
+    return out
+
+
+def cpu_baseline(cfg, steps, budget_s: float):
+    """Time the CPU oracle's record-replay decode on whole requests (every head, beam and step)."""
+    import oracle
+    from linear_attention_beam_amd import inputs
+    try:
+        import threadpoolctl
+        blas_threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                            if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+
+    def head_steps(r, h):
+        f = inputs.bf16_bits_to_f32 if cfg.qkv_dtype == "bf16" else (lambda x: x)
+        return [dict(q=f(s.q[r, :, h])[None, :, None], k=f(s.k[r, :, h])[None, :, None],
+                     v=f(s.v[r, :, h])[None, :, None], alpha=s.alpha[r, :, h][None, :, None],
+                     beta=s.beta[r, :, h][None, :, None], parent=s.parent[r][None]) for s in steps]
+
+    elapsed, reqs, t_start = 0.0, 0, time.time()
+    while reqs < cfg.R and (reqs == 0 or time.time() - t_start < budget_s):
+        r = reqs
+        if cfg.prefill_steps:
+            pf = inputs.prefill_inputs(cfg, requests=[r])
+            sctx = [oracle.prefill(pf.k[:, :, h:h + 1], pf.v[:, :, h:h + 1], pf.alpha[:, :, h:h + 1],
+                                   pf.beta[:, :, h:h + 1])[0, 0] for h in range(cfg.H)]
+        else:
+            sctx = list(inputs.direct_sctx(cfg)[r])
+        hs = [head_steps(r, h) for h in range(cfg.H)]
+        t0 = time.perf_counter()
+        for h in range(cfg.H):
+            oracle.decode_replay(sctx[h][None, None], hs[h], cfg.B, cfg.L)
+        elapsed += time.perf_counter() - t0
+        reqs += 1
+    return {"value": reqs * cfg.B * cfg.L / elapsed, "unit": "beam-tokens/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"requests 0..{reqs - 1} of {cfg.R}: every head, beam and decode step (record-replay form, "
+                      f"float64 numpy; S_ctx from the oracle's own prefill, not timed)",
+            "seconds": round(elapsed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed decodes")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index (default 3: R=32 H=16 B=512 L=8)")
+    ap.add_argument("--tile-beams", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU-baseline work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fullstate", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): the decode shards "
+              "by request or head with no exchange between GPUs, so N GPUs give N independent copies of this "
+              "measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_beam_amd import inputs, onela
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = inputs.config(args.config)
+    log(f"[bench] workload: {cfg.name}")
+    t0 = time.time()
+    steps = inputs.decode_inputs(cfg)
+    pf = inputs.prefill_inputs(cfg) if cfg.prefill_steps else None
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    dsteps = [dict(q=up(s.q), k=up(s.k), v=up(s.v), alpha=up(s.alpha), beta=up(s.beta), parent=up(s.parent))
+              for s in steps]
+    outs = [torch.empty((cfg.R, cfg.B, cfg.H, cfg.d_v), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
+
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype,
+                      tile_beams=args.tile_beams, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    if pf is not None:
+        ctx.prefill(up(pf.k), up(pf.v), up(pf.alpha), up(pf.beta))
+    else:
+        ctx.set_context(up(inputs.direct_sctx(cfg)))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    context_ms = e0.elapsed_time(e1)
+    log(f"[bench] context ready ({'prefill ' + str(cfg.prefill_steps) + ' tokens' if pf else 'set_context'}: "
+        f"{context_ms:.2f} ms)")
+
+    def decode(events=None):
+        ctx.reset()
+        for t in range(cfg.L):
+            if events is not None:
+                events[t][0].record(stream)
+            ctx.step(**dsteps[t], out=outs[t])
+            if events is not None:
+                events[t][1].record(stream)
+
+    for _ in range(args.warmup):
+        decode()
+    torch.cuda.synchronize()
+    if ctx.status() != onela.ONELA_OK:
+        raise RuntimeError("device flag: parent index out of range")
+    view = ctx.view()
+    chains = view["chains"].cpu().numpy()
+    per_launch_bytes = algorithmic_bytes(cfg, chains, [s.parent for s in steps])
+    log(f"[bench] warmup done; algorithmic bytes per decode {sum(per_launch_bytes) / 1e9:.3f} GB")
+
+    launch_events = [[[ev(), ev()] for _ in range(cfg.L)] for _ in range(args.steps)]
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        decode(launch_events[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    kernel_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in launch_events])  # [K, L]
+    kernel_avg_ms = float(kernel_ms.mean())
+    achieved = sum(per_launch_bytes) / (kernel_ms.sum(axis=1).mean() * 1e-3) / 1e9
+    value = cfg.beam_tokens / (ms_per_step * 1e-3)
+    log(f"[bench] {args.steps} decodes: {ms_per_step:.4f} ms/decode (wall {wall / args.steps * 1e3:.4f}), "
+        f"{value:.4g} beam-tokens/s; fused kernel avg {kernel_avg_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+    per_step_us = [round(float(x) * 1e3, 2) for x in kernel_ms.mean(axis=0)]
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        key = f"config{args.config}"
+        if tr.get("kernel_hash") == kernel_source_hash() and key in tr.get("configs", {}):
+            traffic = tr["configs"][key]["bytes_per_launch"]
+    mfma_flops = 8.0 * cfg.d_v * cfg.d_k * cfg.R * cfg.B * cfg.H * cfg.L   # (k and q) x (hi and lo) x 2 flops
+    line = {
+        "metric": "beam-tokens/sec of GDN beam-decode step",
+        "value": value,
+        "unit": "beam-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.qkv_dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": cfg.R, "heads": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
+                   "beams": cfg.B, "decode_steps": cfg.L, "prefill_tokens": cfg.prefill_steps,
+                   "beam_tokens_per_step": cfg.beam_tokens, "tile_beams": args.tile_beams or "auto"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (sum(traffic) / len(traffic)) if traffic else None,
+                     "kernel": "onela::step_fused_kernel",
+                     "algorithmic_bytes_per_launch": sum(per_launch_bytes) / cfg.L,
+                     "kernel_avg_us": kernel_avg_ms * 1e3, "kernel_us_by_decode_step": per_step_us,
+                     "mfma_frac": mfma_flops / (kernel_ms.sum(axis=1).mean() * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+        "context_ms": context_ms,
+    }
+    sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
+    del view
+    ctx.close()
+    del ctx
+
+    if not args.no_fullstate:
+        fs = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, mode="fullstate",
+                         device=dev)
+        fs.set_context(torch.from_numpy(sctx_host).to(dev))
+
+        def fs_decode():
+            fs.reset()
+            for t in range(cfg.L):
+                fs.step(**dsteps[t], out=outs[t])
+
+        fs_decode()
+        torch.cuda.synchronize()
+        reps = 3
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fs_decode()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fs_ms = a.elapsed_time(b) / reps
+        fs_bytes = 2.0 * cfg.R * cfg.B * cfg.H * cfg.d_k * cfg.d_v * 4 * cfg.L
+        line["fullstate"] = {"ms_per_step": fs_ms, "beam_tokens_per_s": cfg.beam_tokens / (fs_ms * 1e-3),
+                             "state_bytes_per_decode": fs_bytes,
+                             "achieved_GBs": fs_bytes / (fs_ms * 1e-3) / 1e9,
+                             "replay_speedup": fs_ms / ms_per_step}
+        log(f"[bench] FullState: {fs_ms:.3f} ms/decode; replay is {fs_ms / ms_per_step:.1f}x faster")
+        fs.close()
+        del fs
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, steps, args.cpu_budget)
+        log(f"[bench] CPU oracle: {line['cpu_baseline']['value']:.4g} beam-tokens/s "
+            f"({line['cpu_baseline']['sample']})")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,13 +20,18 @@ Recipe (every configuration):
   * S_ctx: either N(0, std^2) directly, or the inputs of a prefill of N GDN steps from the zero state
     with the same k/v/alpha/beta distributions (float32, not rounded).  Turning those prefill inputs
     into S_ctx is GDN arithmetic and is done by the caller (the oracle's prefill or the GPU prefill).
-  * Streams: numpy PCG64 seeded by SeedSequence([0x0E1A, config index, stream, seed]); stream 0 draws
-    S_ctx or the prefill inputs, stream 1 the per-step decode inputs, stream 2 the parents.
+  * Streams: numpy PCG64 generators seeded by SeedSequence([0x0E1A, config index, stream, seed, ...]):
+    stream 0 draws S_ctx (one generator) or the prefill inputs (one generator per request, drawing
+    k, v, alpha, beta in that order); stream 1 the decode inputs (one generator per step and request,
+    drawing q, k, v, alpha, beta); stream 2 the parents (one generator per step).  Chunks are drawn in
+    parallel threads; the values do not depend on the thread count.
 """
 
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import List, Optional
 
 import numpy as np
@@ -104,8 +109,12 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(cfg: Config, stream: int, seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([_SEED_TAG, cfg.index, stream, seed])))
+def _rng(cfg: Config, stream: int, seed: int, *chunk: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([_SEED_TAG, cfg.index, stream, seed, *chunk])))
+
+
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _unit_rows_f32(rng: np.random.Generator, shape) -> np.ndarray:
@@ -156,22 +165,30 @@ def parents_for_step(cfg: Config, rng: np.random.Generator, t: int, b_prev: int,
 def decode_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None) -> List[StepInputs]:
     """All decode-step inputs of one configuration (``steps`` defaults to cfg.L)."""
     steps = cfg.L if steps is None else steps
-    rng = _rng(cfg, 1, seed)
-    prng = _rng(cfg, 2, seed)
     R, B, H = cfg.R, cfg.B, cfg.H
+    bf16 = cfg.qkv_dtype == "bf16"
+    enc = f32_to_bf16_bits if bf16 else (lambda x: x)
+    dt = np.uint16 if bf16 else np.float32
     out = []
-    b_prev = 1
     for t in range(1, steps + 1):
-        q = _unit_rows_f32(rng, (R, B, H, cfg.d_k))
-        k = _unit_rows_f32(rng, (R, B, H, cfg.d_k))
-        v = rng.standard_normal((R, B, H, cfg.d_v), dtype=np.float32)
-        alpha = rng.uniform(cfg.alpha_lo, 1.0, size=(R, B, H)).astype(np.float32)
-        beta = rng.uniform(0.0, 1.0, size=(R, B, H)).astype(np.float32)
-        parent = parents_for_step(cfg, prng, t, b_prev, B)
-        if cfg.qkv_dtype == "bf16":
-            q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+        q = np.empty((R, B, H, cfg.d_k), dt)
+        k = np.empty((R, B, H, cfg.d_k), dt)
+        v = np.empty((R, B, H, cfg.d_v), dt)
+        alpha = np.empty((R, B, H), np.float32)
+        beta = np.empty((R, B, H), np.float32)
+
+        def fill(r, t=t, q=q, k=k, v=v, alpha=alpha, beta=beta):
+            rng = _rng(cfg, 1, seed, t, r)
+            q[r] = enc(_unit_rows_f32(rng, (B, H, cfg.d_k)))
+            k[r] = enc(_unit_rows_f32(rng, (B, H, cfg.d_k)))
+            v[r] = enc(rng.standard_normal((B, H, cfg.d_v), dtype=np.float32))
+            alpha[r] = rng.uniform(cfg.alpha_lo, 1.0, size=(B, H))
+            beta[r] = rng.uniform(0.0, 1.0, size=(B, H))
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(R)))
+        parent = parents_for_step(cfg, _rng(cfg, 2, seed, t), t, 1 if t == 1 else B, B)
         out.append(StepInputs(q, k, v, alpha, beta, parent, cfg.qkv_dtype))
-        b_prev = B
     return out
 
 
@@ -196,13 +213,24 @@ class PrefillInputs:
     beta: np.ndarray
 
 
-def prefill_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None) -> PrefillInputs:
-    """Random prompt of ``steps`` (default cfg.prefill_steps) GDN steps for every request and head."""
+def prefill_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None, requests=None) -> PrefillInputs:
+    """Random prompt of ``steps`` (default cfg.prefill_steps) GDN steps for every head of the given
+    requests (default: all), arrays indexed by position in ``requests``."""
     n = cfg.prefill_steps if steps is None else steps
-    rng = _rng(cfg, 0, seed)
-    R, H = cfg.R, cfg.H
-    k = _unit_rows_f32(rng, (R, n, H, cfg.d_k))
-    v = rng.standard_normal((R, n, H, cfg.d_v), dtype=np.float32)
-    alpha = rng.uniform(cfg.alpha_lo, 1.0, size=(R, n, H)).astype(np.float32)
-    beta = rng.uniform(0.0, 1.0, size=(R, n, H)).astype(np.float32)
+    reqs = list(range(cfg.R)) if requests is None else list(requests)
+    H = cfg.H
+    k = np.empty((len(reqs), n, H, cfg.d_k), np.float32)
+    v = np.empty((len(reqs), n, H, cfg.d_v), np.float32)
+    alpha = np.empty((len(reqs), n, H), np.float32)
+    beta = np.empty((len(reqs), n, H), np.float32)
+
+    def fill(i):
+        rng = _rng(cfg, 0, seed, reqs[i])
+        k[i] = _unit_rows_f32(rng, (n, H, cfg.d_k))
+        v[i] = rng.standard_normal((n, H, cfg.d_v), dtype=np.float32)
+        alpha[i] = rng.uniform(cfg.alpha_lo, 1.0, size=(n, H))
+        beta[i] = rng.uniform(0.0, 1.0, size=(n, H))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(len(reqs))))
     return PrefillInputs(k, v, alpha, beta)

@@ -1,0 +1,185 @@
+"""GPU edge cases against the oracle: ragged and varying beam counts, every fused tile size and d_v,
+request x head counts that are not a multiple of the 8 XCDs, 64-step chains, determinism, a parent out of
+range, host-side argument and state errors, reset and reuse."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_beam_amd import inputs, onela
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def ragged_steps(steps, beams):
+    """Keep beams[t] beams at step t; parents of kept beams are folded into the previous step's range."""
+    out = []
+    b_prev = 1
+    for s, n in zip(steps, beams):
+        par = (s.parent[:, :n] % b_prev).astype(np.int32)
+        out.append(inputs.StepInputs(np.ascontiguousarray(s.q[:, :n]), np.ascontiguousarray(s.k[:, :n]),
+                                     np.ascontiguousarray(s.v[:, :n]), np.ascontiguousarray(s.alpha[:, :n]),
+                                     np.ascontiguousarray(s.beta[:, :n]), par, s.dtype))
+        b_prev = n
+    return out
+
+
+def short_prefill_sctx(cfg, tokens=48):
+    pf = inputs.prefill_inputs(cfg, steps=tokens)
+    return oracle.prefill(pf.k, pf.v, pf.alpha, pf.beta)
+
+
+def check_all_heads(run, cfg, steps, sctx, max_beams, max_steps, check_records=True):
+    chains = gu.all_chains(steps, max_beams, max_steps, cfg.R)
+    worst = 0.0
+    for r in range(cfg.R):
+        for h in range(cfg.H):
+            ref, _ = gu.oracle_head(sctx[r, h], steps, r, h, max_beams, max_steps)
+            e_o, _ = gu.compare_head(run, steps, ref, chains[r], r, h, check_records=check_records)
+            worst = max(worst, e_o)
+    return worst
+
+
+RAGGED = [1, 37, 100, 64, 99]
+
+
+@pytest.mark.parametrize("d_v,tile,generic", [
+    (128, 16, False), (128, 32, False), (128, 64, False), (128, 128, False), (64, 0, False), (256, 0, False),
+    (32, 128, False), (96, 32, False), (128, 0, True),
+])
+def test_ragged_beams(d_v, tile, generic):
+    cfg = inputs.config(2, R=3, H=5, d_v=d_v, B=100, L=len(RAGGED))
+    gu.log(f"ragged beams {RAGGED} d_v={d_v} tile={tile} generic={generic} (R*H=15)")
+    steps = ragged_steps(inputs.decode_inputs(cfg), RAGGED)
+    sctx = short_prefill_sctx(cfg)
+    try:
+        run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile, force_generic=generic, max_beams=128, max_steps=6)
+    except onela.OnelaError as e:
+        if e.status == onela.ONELA_ERR_UNSUPPORTED:
+            pytest.skip(f"device LDS limit: {e}")
+        raise
+    assert run.view["fused"] == (not generic)
+    assert run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
+
+
+def test_tiles_and_xcd_mapping_agree():
+    """R*H = 16 (a multiple of 8, XCD-grouped mapping) and every tile size give the same outputs."""
+    cfg = inputs.config(2, R=2, H=8, B=96, L=3)
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    runs = [gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=t) for t in (16, 32, 64, 128)]
+    for run in runs[1:]:
+        for t in range(cfg.L):
+            assert (run.outs[t] - runs[0].outs[t]).abs().max().item() <= 1e-6
+    gu.log(f"  max|o err|={check_all_heads(runs[2], cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_64_step_chains(generic):
+    cfg = inputs.config(1, R=1, H=2, d_v=32, B=16, L=64)
+    gu.log(f"64 steps, generic={generic}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, force_generic=generic)
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
+def test_deterministic():
+    cfg = inputs.config(2, R=2, H=4, B=256, L=4)
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    a = gu.GpuRun(cfg, steps, sctx=sctx)
+    b = gu.GpuRun(cfg, steps, sctx=sctx)
+    for t in range(cfg.L):
+        assert torch.equal(a.outs[t], b.outs[t])
+    assert torch.equal(a.view["rec_u"], b.view["rec_u"])
+
+
+@pytest.mark.parametrize("mode", ["replay", "fullstate"])
+def test_parent_out_of_range_is_flagged(mode):
+    cfg = inputs.config(2, R=2, H=2, B=32, L=3)
+    steps = inputs.decode_inputs(cfg)
+    bad = [inputs.StepInputs(s.q, s.k, s.v, s.alpha, s.beta, s.parent.copy(), s.dtype) for s in steps]
+    bad[1].parent[1, 5] = cfg.B          # out of range in request 1 only
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, bad, sctx=sctx, mode=mode)
+    assert run.status == onela.ONELA_ERR_BAD_PARENT
+    chains = gu.all_chains(steps[:1], cfg.B, cfg.L, cfg.R)
+    for h in range(cfg.H):               # request 0 is untouched by request 1's bad index
+        ref, _ = gu.oracle_head(sctx[0, h], bad, 0, h, cfg.B, cfg.L)
+        for t in range(cfg.L):
+            assert np.max(np.abs(run.head_o(t, 0, h) - ref["o"][t])) <= gu.TOL
+    assert np.array_equal(run.view["chains"][0, 0].cpu().numpy(), chains[0][0])
+    run.ctx.reset()
+    assert run.ctx.status() == onela.ONELA_OK
+
+
+def test_host_errors_leave_state_unchanged():
+    cfg = inputs.config(2, R=1, H=2, B=8, L=2)
+    steps = inputs.decode_inputs(cfg)
+    dev = gu.device()
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, 2, device=dev)
+    d = gu.upload_step(steps[0], dev)
+    with pytest.raises(onela.OnelaError) as e:       # no context yet
+        ctx.step(**d)
+    assert e.value.status == onela.ONELA_ERR_STATE
+    ctx.set_context(torch.zeros((1, 2, 128, 128), device=dev))
+    h, s = ctx.handle, torch.cuda.current_stream().cuda_stream
+    ptrs = [d[k].data_ptr() for k in ("q", "k", "v", "alpha", "beta", "parent")]
+    o = torch.empty((1, 8, 2, 128), device=dev)
+    for n_beams in (0, 9):
+        st = onela.lib().onela_step(h, n_beams, *ptrs, o.data_ptr(), s)
+        assert st == onela.ONELA_ERR_INVALID_ARG
+    st = onela.lib().onela_step(h, 8, *ptrs[:2], None, *ptrs[3:], o.data_ptr(), s)
+    assert st == onela.ONELA_ERR_INVALID_ARG
+    assert onela.onela_get_view(h).t == 0
+    ctx.step(**d)
+    ctx.step(**gu.upload_step(steps[1], dev))
+    with pytest.raises(onela.OnelaError) as e:       # both steps of the context are used
+        ctx.step(**gu.upload_step(steps[1], dev))
+    assert e.value.status == onela.ONELA_ERR_CAPACITY
+    assert onela.onela_get_view(h).t == 2
+    with pytest.raises(ValueError):                  # wrong dtype is caught by the binding
+        ctx.step(d["q"].float(), d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+    bad_ws = torch.empty(1024, dtype=torch.uint8, device=dev)
+    with pytest.raises(onela.OnelaError) as e:
+        onela.onela_create(ctx.cfg, bad_ws.data_ptr(), 1024)
+    assert e.value.status == onela.ONELA_ERR_CAPACITY
+    ctx.close()
+
+
+def test_reset_and_reuse():
+    """A second decode on the same context after reset matches the oracle (records are overwritten)."""
+    cfg = inputs.config(2, R=2, H=3, B=48, L=3)
+    sctx = short_prefill_sctx(cfg)
+    first = inputs.decode_inputs(cfg, seed=1)
+    second = inputs.decode_inputs(cfg, seed=2)
+    dev = gu.device()
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, device=dev)
+    ctx.set_context(torch.from_numpy(sctx.astype(np.float32)).to(dev))
+    for s in first:
+        ctx.step(**gu.upload_step(s, dev))
+    ctx.reset()
+    outs = [ctx.step(**gu.upload_step(s, dev)) for s in second]
+    torch.cuda.synchronize()
+    for r in range(cfg.R):
+        for h in range(cfg.H):
+            ref, _ = gu.oracle_head(sctx[r, h], second, r, h, cfg.B, cfg.L)
+            for t in range(cfg.L):
+                got = outs[t][r, :, h].double().cpu().numpy()
+                assert np.max(np.abs(got - ref["o"][t])) <= gu.TOL
+
+
+def test_context_transpose_is_exact():
+    cfg = inputs.config(2, R=2, H=3, B=8, L=1)
+    sctx = np.random.default_rng(5).standard_normal((2, 3, 128, 128)).astype(np.float32)
+    dev = gu.device()
+    ctx = onela.OneLA(cfg.R, cfg.H, 128, 128, 8, 1, device=dev)
+    ctx.set_context(torch.from_numpy(sctx).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(ctx.view()["sctx_t"].cpu().numpy(), np.swapaxes(sctx, -1, -2))

@@ -1,0 +1,130 @@
+"""GPU parity: libonela's decode against the CPU oracle on the same seeded inputs.
+
+Small configurations are compared on every (request, head); the full-size ones (the launch shapes the
+benchmark times) on sampled heads, end to end from the GPU prefill, with every request's chain table
+compared in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_beam_amd import inputs, onela
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_sctx_all(cfg, pf):
+    return oracle.prefill(pf.k, pf.v, pf.alpha, pf.beta)
+
+
+# --------------------------------------------------------------------------------------------------
+# Tiny configuration (fp32, every element)
+# --------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["replay", "fullstate"])
+def test_tiny_config(mode):
+    cfg = inputs.config(0)
+    gu.log(f"tiny config, mode={mode}")
+    sctx = inputs.direct_sctx(cfg)
+    steps = inputs.decode_inputs(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, mode=mode)
+    assert run.status == onela.ONELA_OK
+    assert not run.view["fused"]
+    chains = gu.all_chains(steps, cfg.B, cfg.L, cfg.R)
+    ref, _ = gu.oracle_head(sctx[0, 0], steps, 0, 0, cfg.B, cfg.L)
+    e_o, e_u = gu.compare_head(run, steps, ref, chains[0], 0, 0, check_records=mode == "replay")
+    gu.log(f"  max|o err|={e_o:.3g} max|u err|={e_u:.3g}")
+    # fp32 arithmetic on both sides of a float64 reference: far inside the bar
+    assert e_o < 1e-5
+
+
+# --------------------------------------------------------------------------------------------------
+# R=1 H=16 d=128 B=128 L=4: every head, oracle-prefilled S_ctx, all three kernels
+# --------------------------------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c1():
+    cfg = inputs.config(1)
+    pf = inputs.prefill_inputs(cfg)
+    sctx = _oracle_sctx_all(cfg, pf)
+    steps = inputs.decode_inputs(cfg)
+    refs = {(0, h): gu.oracle_head(sctx[0, h], steps, 0, h, cfg.B, cfg.L)[0] for h in range(cfg.H)}
+    chains = gu.all_chains(steps, cfg.B, cfg.L, cfg.R)
+    return cfg, pf, sctx, steps, refs, chains
+
+
+@pytest.mark.parametrize("variant", ["fused", "generic", "fullstate"])
+def test_c1_every_head(c1, variant):
+    cfg, pf, sctx, steps, refs, chains = c1
+    gu.log(f"R=1 H=16 B=128 L=4, variant={variant}")
+    run = gu.GpuRun(cfg, steps, sctx=sctx, mode="fullstate" if variant == "fullstate" else "replay",
+                    force_generic=variant == "generic")
+    assert run.view["fused"] == (variant == "fused")
+    assert run.status == onela.ONELA_OK
+    worst = (0.0, 0.0)
+    for h in range(cfg.H):
+        e = gu.compare_head(run, steps, refs[(0, h)], chains[0], 0, h, check_records=variant != "fullstate")
+        worst = tuple(max(a, b) for a, b in zip(worst, e))
+    gu.log(f"  max|o err|={worst[0]:.3g} max|u err|={worst[1]:.3g}")
+
+
+def test_c1_fused_matches_fp32_kernel(c1):
+    """The bf16 high/low MFMA contraction against the plain fp32-FMA kernel on the same inputs: the
+    split keeps 16 significand bits of S_ctx, so the two agree far inside the oracle bar."""
+    cfg, pf, sctx, steps, refs, chains = c1
+    a = gu.GpuRun(cfg, steps, sctx=sctx)
+    b = gu.GpuRun(cfg, steps, sctx=sctx, force_generic=True)
+    for t in range(cfg.L):
+        d = (a.outs[t] - b.outs[t]).abs().max().item()
+        assert d < 1e-4, (t, d)
+
+
+def test_prefill_matches_oracle(c1):
+    """GPU prefill (float32, 1024 tokens) against the float64 oracle prefill, every head."""
+    cfg, pf, sctx, steps, refs, chains = c1
+    run = gu.GpuRun(cfg, steps[:1], prefill=pf, sctx_out=True, max_steps=cfg.L)
+    got = run.sctx_gpu.double().cpu().numpy()
+    err = float(np.max(np.abs(got - sctx)))
+    gu.log(f"  prefill max|S err|={err:.3g} (max|S|={np.max(np.abs(sctx)):.3g})")
+    assert err < 2e-4
+    st = run.view["sctx_t"].double().cpu().numpy()
+    assert np.array_equal(st, np.swapaxes(got, -1, -2))
+
+
+# --------------------------------------------------------------------------------------------------
+# Full-size configurations, as the benchmark runs them: GPU prefill, then the decode
+# --------------------------------------------------------------------------------------------------
+
+def _sample_heads(cfg):
+    rng = np.random.default_rng(1234 + cfg.index)
+    pick = {(0, 0), (cfg.R - 1, cfg.H - 1), (cfg.R // 2, 1 % cfg.H)}
+    while len(pick) < 5:
+        pick.add((int(rng.integers(cfg.R)), int(rng.integers(cfg.H))))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("ci", [2, 3, 4])
+def test_full_size(ci):
+    cfg = inputs.config(ci)
+    gu.log(f"full size: {cfg.name}")
+    pf = inputs.prefill_inputs(cfg)
+    steps = inputs.decode_inputs(cfg)
+    run = gu.GpuRun(cfg, steps, prefill=pf, sctx_out=True)
+    assert run.status == onela.ONELA_OK
+    assert run.view["fused"]
+    chains = gu.all_chains(steps, cfg.B, cfg.L, cfg.R)
+    for r in range(cfg.R):       # every request's ancestry index, bit for bit
+        for t in range(cfg.L):
+            assert np.array_equal(run.view["chains"][t, r].cpu().numpy(), chains[r][t]), (r, t)
+    worst = [0.0, 0.0, 0.0]
+    for r, h in _sample_heads(cfg):
+        s_ref = gu.oracle_prefill_head(pf, r, h)
+        s_err = float(np.max(np.abs(run.sctx_gpu[r, h].double().cpu().numpy() - s_ref)))
+        assert s_err < 2e-4, (r, h, s_err)
+        ref, _ = gu.oracle_head(s_ref, steps, r, h, cfg.B, cfg.L)
+        e = gu.compare_head(run, steps, ref, chains[r], r, h)
+        worst = [max(worst[0], e[0]), max(worst[1], e[1]), max(worst[2], s_err)]
+    gu.log(f"  sampled heads: max|o err|={worst[0]:.3g} max|u err|={worst[1]:.3g} max|S err|={worst[2]:.3g}")
