@@ -80,10 +80,10 @@ hipError_t launch_transpose_sctx(const float* S, float* ST, int RH, int d_v, int
 }
 
 // ---------------------------------------------------------------------------------------------------
-// bf16 high/low split of S_ctx in the operand order of the fused kernel's MFMA (B operand of
-// v_mfma_f32_16x16x32_bf16, lane l holding rows 8*(l/16)..+7 of column l%16).
-// Per (request, head): [hl 2][w d_v/32][ks d_k/32][n 2][lane 64][e 8] bf16 with
-//   value = S[dv = 32 w + 2 (lane % 16) + n][dk = 32 ks + 8 (lane / 16) + e],
+// bf16 high/low split of S_ctx in the operand order of the fused kernel's MFMA (A operand of
+// v_mfma_f32_16x16x32_bf16: lane l holds row l%16, columns 8*(l/16)..+7 of a 16x32 block).
+// Per (request, head): [hl 2][w d_v/32][ks d_k/32][mi 2][lane 64][e 8] bf16 with
+//   value = S[dv = 32 w + 16 mi + lane % 16][dk = 32 ks + 8 (lane / 16) + e],
 //   hi = RNE_bf16(x), lo = RNE_bf16(x - hi), so hi + lo carries 16 significant bits of x.
 // One thread per 8-element fragment.
 // ---------------------------------------------------------------------------------------------------
@@ -97,11 +97,11 @@ __global__ void split_frag_kernel(const float* __restrict__ ST, uint16_t* __rest
   size_t f = idx - (size_t)rh * per_rh;
   const int lane = (int)(f & 63);
   f >>= 6;
-  const int n = (int)(f & 1);
+  const int mi = (int)(f & 1);
   f >>= 1;
   const int ks = (int)(f % KS);
   const int w = (int)(f / KS);
-  const int dv = 32 * w + 2 * (lane & 15) + n;
+  const int dv = 32 * w + 16 * mi + (lane & 15);
   const int dk0 = 32 * ks + 8 * (lane >> 4);
   const float* src = ST + (size_t)rh * d_k * d_v;
   uint32_t hi[8], lo[8];
@@ -114,7 +114,7 @@ __global__ void split_frag_kernel(const float* __restrict__ ST, uint16_t* __rest
   h4.x = hi[0] | (hi[1] << 16); h4.y = hi[2] | (hi[3] << 16); h4.z = hi[4] | (hi[5] << 16); h4.w = hi[6] | (hi[7] << 16);
   l4.x = lo[0] | (lo[1] << 16); l4.y = lo[2] | (lo[3] << 16); l4.z = lo[4] | (lo[5] << 16); l4.w = lo[6] | (lo[7] << 16);
   uint16_t* base = frag + (size_t)rh * 2 * per_rh * 8;
-  const size_t off = (((size_t)w * KS + ks) * 2 + n) * 64 + lane;
+  const size_t off = (((size_t)w * KS + ks) * 2 + mi) * 64 + lane;
   *reinterpret_cast<u32x4_t*>(base + off * 8) = h4;
   *reinterpret_cast<u32x4_t*>(base + (per_rh + off) * 8) = l4;
 }

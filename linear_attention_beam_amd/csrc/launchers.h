@@ -25,6 +25,8 @@ struct StepArgs {
   const int32_t* parent;      // [R][n]
   const int32_t* chain_prev;  // table after step t-1, NULL at t = 1
   int32_t* chain_out;         // table after step t
+  const float* decay_prev;    // fused kernel: [R][H][B_max][L_max + 1] decays along each chain after step t-1
+  float* decay_out;           //   (c_0 .. c_{L_max-1}, then A); this step's rows
   int* flag;                  // set to `epoch` when a parent index is out of range
   int epoch;
   int b_prev;
@@ -45,7 +47,7 @@ hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Fused bf16-MFMA step (d_k == 128, d_v % 32 == 0, d_v <= 256).  tile_beams 0 = automatic.
 bool fused_supported(int d_k, int d_v, int L_max);
 int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested);
-size_t fused_lds_bytes(int tile, int L_max);
+size_t fused_lds_bytes(int tile, int L_max, int d_v);
 hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s);
 
 hipError_t launch_fullstate(const StepArgs& a, bool bf16, const int32_t* parent, int b_prev, const float* fs_prev,

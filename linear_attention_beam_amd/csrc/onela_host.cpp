@@ -8,7 +8,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/onela.h"
+#include "onela.h"
 #include "launchers.h"
 
 using namespace onela;
@@ -23,6 +23,7 @@ struct onela_ctx {
   float* sctx_t;
   uint16_t* sctx_frag;
   int32_t* chains;
+  float* decay;  // fused path: [2][R][H][B_max][L_max + 1], step t writes buffer t % 2
   void* rec_k;
   float* rec_u;
   float* rec_alpha;
@@ -54,7 +55,7 @@ onela_status ok() {
 }
 
 struct Layout {
-  size_t flag, sctx_t, sctx_frag, chains, rec_k, rec_u, rec_alpha, fullstate, total;
+  size_t flag, sctx_t, sctx_frag, chains, decay, rec_k, rec_u, rec_alpha, fullstate, total;
   bool fused;
 };
 
@@ -99,6 +100,7 @@ Layout make_layout(const onela_config* c) {
   l.sctx_t = off;     off = align256(off + R * H * dk * dv * 4);
   l.sctx_frag = off;  off = align256(off + (l.fused ? R * H * dk * dv * 2 * 2 : 0));
   l.chains = off;     off = align256(off + L * R * B * L * 4);
+  l.decay = off;      off = align256(off + (l.fused ? 2 * R * H * B * (L + 1) * 4 : 0));
   if (c->mode == ONELA_MODE_REPLAY) {
     l.rec_k = off;     off = align256(off + R * H * slots * dk * in_bytes);
     l.rec_u = off;     off = align256(off + R * H * slots * dv * 4);
@@ -183,6 +185,7 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
   h->sctx_t = reinterpret_cast<float*>(ws + l.sctx_t);
   h->sctx_frag = l.fused ? reinterpret_cast<uint16_t*>(ws + l.sctx_frag) : nullptr;
   h->chains = reinterpret_cast<int32_t*>(ws + l.chains);
+  h->decay = l.fused ? reinterpret_cast<float*>(ws + l.decay) : nullptr;
   if (cfg->mode == ONELA_MODE_REPLAY) {
     h->rec_k = ws + l.rec_k;
     h->rec_u = reinterpret_cast<float*>(ws + l.rec_u);
@@ -256,9 +259,9 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
   int tile = 0;
   if (c.mode == ONELA_MODE_REPLAY && h->fused) {
     tile = fused_pick_tile(c.num_requests, c.num_heads, n_beams, c.d_v, c.max_steps, c.tile_beams);
-    if (fused_lds_bytes(tile, c.max_steps) > (size_t)h->max_lds)
+    if (fused_lds_bytes(tile, c.max_steps, c.d_v) > (size_t)h->max_lds)
       return fail(ONELA_ERR_UNSUPPORTED, "tile_beams %d with max_steps %d needs %zu bytes of LDS, the device allows %d",
-                  tile, c.max_steps, fused_lds_bytes(tile, c.max_steps), h->max_lds);
+                  tile, c.max_steps, fused_lds_bytes(tile, c.max_steps, c.d_v), h->max_lds);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = h->t + 1;
@@ -280,6 +283,11 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
   a.chain = chain_out;
   a.parent = d_parent_idx; a.chain_prev = chain_prev; a.chain_out = chain_out;
   a.flag = h->flag; a.epoch = h->epoch; a.b_prev = h->n_beams;
+  if (h->decay) {
+    const size_t dbuf = (size_t)c.num_requests * c.num_heads * c.max_beams * (c.max_steps + 1);
+    a.decay_prev = h->decay + (size_t)((t - 1) & 1) * dbuf;
+    a.decay_out = h->decay + (size_t)(t & 1) * dbuf;
+  }
   a.R = c.num_requests; a.H = c.num_heads; a.d_k = c.d_k; a.d_v = c.d_v; a.n = n_beams;
   a.B_max = c.max_beams; a.L_max = c.max_steps; a.slots = c.max_beams * c.max_steps; a.t = t;
   const bool bf16 = c.qkv_dtype == ONELA_BF16;

@@ -1,21 +1,22 @@
-// Fused projection-replay decode step for gfx950: bf16 MFMA contraction of the shared state, record
-// replay and record append in one kernel ("Scientific Impact Assessment: OneLA", §1: a fused GPU kernel
-// reuses S_ctx across beams; paper index page, Abstract).
+// Fused projection-replay decode step for gfx950: ancestry update, bf16 MFMA contraction of the shared
+// state, record replay and record append in one kernel ("Scientific Impact Assessment: OneLA", §1: a fused
+// GPU kernel reuses S_ctx across beams; paper index page, Abstract).
 //
 // Workgroup = (request, head, tile of NB beams); d_v / 32 waves of 64 lanes (d_k = 128 fixed).
-//   Phase 0  ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each beam's chain is
-//            its parent's chain from the previous table plus its own slot; the head-0 workgroups write
-//            the new table.  Stage k and q of the tile in LDS; read the chain records' alphas and form
-//            the decays A = prod alpha and c_j = prod of the alphas after record j.
-//   Phase 1  (16 lanes per beam) dot products of the chain keys with k and q, and k . q, reduced with
-//            DPP inside a 16-lane row; append the record key and alpha.
-//   Phase 2  each wave owns 32 columns of d_v.  For 16 beams at a time it runs
-//            v_mfma_f32_16x16x32_bf16 over d_k: [P_k | P_q] = X^T S_ctx^T with X = [k | q], in two
-//            passes over the bf16 high and low halves of S_ctx (the halves stay in registers for the
-//            whole tile: each S_ctx element is read once per tile and reused by all NB beams).  The
-//            accumulator layout (lane l: beam 4(l/16)+i, column l%16) is used as is: with the columns of
-//            S_ctx^T permuted at split time, lane l holds d_v elements 32 w + 2 (l%16) + {0, 1}, so the
-//            replay reads each record's u as contiguous float2 and writes u and o the same way:
+//   Phase 0  ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each beam's chain is its
+//            parent's chain from the previous table plus its own slot; the head-0 workgroups write the new
+//            table.  The decays along a chain (A = prod alpha, c_j = prod of the alphas after record j) are
+//            kept per (request, head, beam) next to the index: a beam reads its parent's row, and writes
+//            its own (c_j alpha_b for the parent's records, 1 for its own record, A alpha_b) for the next
+//            step, so no record alpha is gathered.  Stage k and q of the tile in LDS.
+//   Phase 1  (16 lanes per beam) dot products of the chain keys with k and q, and k . q, reduced with DPP
+//            inside a 16-lane row; append the record key and alpha.
+//   Phase 2  wave w owns d_v rows 32w .. 32w+31 of S_ctx, whose bf16 high and low halves stay in registers
+//            for the whole tile (each S_ctx element is read once per tile and reused by all NB beams).
+//            For 16 beams at a time, v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over
+//            d_k, high then low half into one float32 accumulator.  In the accumulator lane l holds beam
+//            l % 16 and d_v rows 4 (l / 16) .. +3 of each 16-row block, so the replay works per beam on
+//            16-byte pieces: two float4 loads of each chain record's u, float4 stores of u and o:
 //              p = A P_k + sum_j c_j (K_j.k) U_j,  u = beta (v - alpha p),
 //              o = alpha (A P_q + sum_j c_j (K_j.q) U_j) + (k.q) u.
 // Workgroups of one (request, head) are mapped to the same XCD (dispatch is round-robin over the 8 XCDs)
@@ -26,26 +27,27 @@
 namespace onela {
 
 namespace {
-constexpr int kDK = 128;          // d_k of the fused kernel
-constexpr int kKS = kDK / 32;     // MFMA k-steps
+constexpr int kDK = 128;             // d_k of the fused kernel
+constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
+constexpr int kItems = 16;           // chain keys in flight per 16-lane group (phase 1)
+constexpr int kChunk = 3;            // chain records in flight per beam (phase 2)
 
 struct FusedLds {
-  int xs, slot, alph, coefk, coefq, beamA, beamAl, beamBe, beamKq, beamPar, total;
+  int xs, slot, alph, coef, beamA, beamAl, beamBe, beamKq, beamPar, total;  // alph: c_j
 };
 
 __host__ __device__ inline FusedLds fused_layout(int NB, int L) {
   FusedLds l;
   int off = 0;
-  l.xs = off;     off += 2 * NB * kXRow;
-  l.slot = off;   off += NB * L * 4;
-  l.alph = off;   off += NB * L * 4;   // chain alphas, then c_j
-  l.coefk = off;  off += NB * L * 4;
-  l.coefq = off;  off += NB * L * 4;
-  l.beamA = off;  off += NB * 4;
-  l.beamAl = off; off += NB * 4;
-  l.beamBe = off; off += NB * 4;
-  l.beamKq = off; off += NB * 4;
+  l.xs = off;      off += 2 * NB * kXRow;  // k rows, then q rows
+  l.slot = off;    off += NB * L * 4;
+  l.alph = off;    off += NB * L * 4;      // c_j
+  l.coef = off;    off += NB * L * 8;      // (c_j (K_j . k), c_j (K_j . q)) pairs
+  l.beamA = off;   off += NB * 4;
+  l.beamAl = off;  off += NB * 4;
+  l.beamBe = off;  off += NB * 4;
+  l.beamKq = off;  off += NB * 4;
   l.beamPar = off; off += NB * 4;
   l.total = off;
   return l;
@@ -55,19 +57,18 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L) {
 template <int NB>
 __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const FusedLds lay = fused_layout(NB, a.L_max);
+  const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
+  const FusedLds lay = fused_layout(NB, L);
   unsigned char* xs = lds + lay.xs;
   int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
   float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
-  float* coefk = reinterpret_cast<float*>(lds + lay.coefk);
-  float* coefq = reinterpret_cast<float*>(lds + lay.coefq);
+  f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
   float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
   float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
   float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
   float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
   int* beamPar = reinterpret_cast<int*>(lds + lay.beamPar);
 
-  const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
 
@@ -87,30 +88,20 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   const int nb = min(NB, n - b0);
   const int nch = a.t - 1;
   const size_t arena = (size_t)rh * a.slots;
-  const uint16_t* qin = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kin = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vin = static_cast<const uint16_t*>(a.v);
-  uint16_t* rec_k = static_cast<uint16_t*>(a.rec_k);
+  const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v);
+  // Records are read only at slots of earlier steps and written only at this step's slots, so the read
+  // and write views never touch the same element.
+  const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k);
+  uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k);
+  const float* __restrict__ u_rd = a.rec_u;
+  float* __restrict__ u_wr = a.rec_u;
+  float* __restrict__ al_wr = a.rec_alpha;
+  float* __restrict__ o_wr = a.o;
   auto in_row = [&](int bb) { return ((size_t)r * n + b0 + bb) * H + h; };
 
-  // ---- this wave's 32 columns of S_ctx^T, bf16 high and low halves, resident for the whole tile ----
-  // fragment file per (request, head): [hl][w][ks][n][lane][8]
-  bf16x8_t sf[kKS][2][2];
-  {
-    const int W = d_v / 32;
-    const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
-    const u32x4_t* fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
-          sf[ks][nn][hl] = __builtin_bit_cast(
-              bf16x8_t, fr[hl * half + (((size_t)wave * kKS + ks) * 2 + nn) * 64 + lane]);
-  }
-
-  // ---- phase 0: parents, stage k and q, chains, chain alphas; per-beam alpha and beta ----
+  // ---- phase 0: parents; stage k and q; chains and their alphas; per-beam alpha and beta ----
   for (int bb = tid; bb < NB; bb += nthreads) {
     const bool live = bb < nb;
     int p = 0;
@@ -129,20 +120,46 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     const int row = idx >> 4, c = idx & 15;  // row < NB: key rows, row >= NB: query rows
     const int bb = row < NB ? row : row - NB;
     u32x4_t val = {0u, 0u, 0u, 0u};
-    if (bb < nb) {
-      const uint16_t* src = (row < NB ? kin : qin) + in_row(bb) * kDK + c * 8;
-      val = *reinterpret_cast<const u32x4_t*>(src);
-    }
+    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + in_row(bb) * kDK + c * 8);
     *reinterpret_cast<u32x4_t*>(xs + row * kXRow + c * 16) = val;
   }
   __syncthreads();
-  for (int idx = tid; idx < nb * nch; idx += nthreads) {
-    const int bb = idx / nch, m = idx - bb * nch;
-    const int raw = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
-    const int s = raw < 0 ? 0 : (raw >= a.slots ? a.slots - 1 : raw);
-    slot_tab[bb * L + m] = s;
-    c_tab[bb * L + m] = a.rec_alpha[arena + s];
-    if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw;
+  const int drow = L + 1;  // decay row: c_0 .. c_{L-1}, then A
+  for (int base = 0; base < nb * nch; base += 4 * nthreads) {
+    int raw[4];
+    float dec[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + u * nthreads + tid;
+      raw[u] = 0;
+      dec[u] = 0.f;
+      if (idx < nb * nch) {
+        const int bb = idx / nch, m = idx - bb * nch;
+        raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
+        dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + u * nthreads + tid;
+      if (idx < nb * nch) {
+        const int bb = idx / nch, m = idx - bb * nch;
+        slot_tab[bb * L + m] = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
+        c_tab[bb * L + m] = dec[u];
+        a.decay_out[((size_t)rh * a.B_max + b0 + bb) * drow + m] = dec[u] * beamAl[bb];
+        if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
+      }
+    }
+  }
+  for (int bb = tid; bb < NB; bb += nthreads) {
+    float A = 0.f;
+    if (bb < nb) {
+      A = nch > 0 ? a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L] : 1.f;
+      float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
+      dout[nch] = 1.f;
+      dout[L] = A * beamAl[bb];
+    }
+    beamA[bb] = A;
   }
   if (h == 0) {  // the rest of each row: own slot, then -1; rows of beams >= n are all -1
     for (int idx = tid; idx < nb * (L - nch); idx += nthreads) {
@@ -155,135 +172,190 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     }
   }
   __syncthreads();
-  for (int bb = tid; bb < NB; bb += nthreads) {  // alphas -> suffix products c_j, and A
-    float run = 1.f;
-    if (bb < nb) {
-      for (int m = nch - 1; m >= 0; --m) {
-        const float al = c_tab[bb * L + m];
-        c_tab[bb * L + m] = run;
-        run *= al;
+
+  // ---- phase 2 gathers: for this lane's beam (col) in beam tile mt, records m0 .. m0+kChunk-1 of its
+  // chain: u at its two 4-row pieces; v at the same rows when m0 == 0.  The first tile's gathers fly
+  // during phase 1.
+  const int gq = lane >> 4, col = lane & 15;
+  const int dv0 = wave * 32 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3 and dv0+16 .. dv0+19
+  f32x4_t U[kChunk][2];
+  f32x2_t V[2];
+  auto gather = [&](int mt, int m0) {
+    const int bb = min(mt * 16 + col, nb - 1);
+    if (m0 == 0) {
+      const uint16_t* vr = vin + in_row(bb) * d_v + dv0;
+      V[0] = *reinterpret_cast<const f32x2_t*>(vr);
+      V[1] = *reinterpret_cast<const f32x2_t*>(vr + 16);
+    }
+    if (nch > 0) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int m = min(m0 + u, nch - 1);
+        const float* ur = u_rd + (arena + slot_tab[bb * L + m]) * d_v + dv0;
+        U[u][0] = *reinterpret_cast<const f32x4_t*>(ur);
+        U[u][1] = *reinterpret_cast<const f32x4_t*>(ur + 16);
       }
     }
-    beamA[bb] = bb < nb ? run : 0.f;
-  }
-  __syncthreads();
+  };
+  gather(0, 0);
 
-  // ---- phase 1: chain-key dot products, 16 lanes per beam; append key and alpha ----
+  // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q; then k . q; append k, alpha ----
+  bf16x8_t sf[kKS][2][2];
   {
     const int g = tid >> 4, j = tid & 15;
     const int ngroups = nthreads >> 4;
+    const int items = nb * nch;
+    for (int it0 = g * kItems; it0 < items; it0 += ngroups * kItems) {
+      const int bb0 = it0 / nch, m00 = it0 - bb0 * nch;
+      u32x4_t K[kItems];
+      {
+        int bb = bb0, m = m00;
+#pragma unroll
+        for (int u = 0; u < kItems; ++u) {
+          const bool valid = it0 + u < items;
+          const int s = slot_tab[(valid ? bb : bb0) * L + (valid ? m : m00)];
+          K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + (arena + s) * kDK + j * 8);
+          if (++m == nch) { m = 0; ++bb; }
+        }
+      }
+      int bb = bb0, m = m00;
+#pragma unroll
+      for (int u = 0; u < kItems; ++u) {
+        if (it0 + u < items) {  // uniform over the 16 lanes of the group
+          const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
+          const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
+          const float dk = row16_sum(dot8_bf16(K[u], kx));
+          const float dq = row16_sum(dot8_bf16(K[u], qx));
+          if (j == 0) {
+            const float c = c_tab[bb * L + m];
+            coef[bb * L + m] = (f32x2_t){c * dk, c * dq};
+          }
+        }
+        if (++m == nch) { m = 0; ++bb; }
+      }
+    }
     for (int bb = g; bb < nb; bb += ngroups) {
       const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
       const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
-      const int own = (a.t - 1) * a.B_max + b0 + bb;
-      *reinterpret_cast<u32x4_t*>(rec_k + (arena + own) * kDK + j * 8) = kx;
       const float kq = row16_sum(dot8_bf16(kx, qx));
-      for (int m0 = 0; m0 < nch; m0 += 4) {
-        u32x4_t K[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int m = m0 + u < nch ? m0 + u : nch - 1;
-          K[u] = *reinterpret_cast<const u32x4_t*>(rec_k + (arena + slot_tab[bb * L + m]) * kDK + j * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float dk = row16_sum(dot8_bf16(K[u], kx));
-          const float dq = row16_sum(dot8_bf16(K[u], qx));
-          if (j == 0 && m0 + u < nch) {
-            const float c = c_tab[bb * L + m0 + u];
-            coefk[bb * L + m0 + u] = c * dk;
-            coefq[bb * L + m0 + u] = c * dq;
-          }
-        }
-      }
+      const int own = nch * a.B_max + b0 + bb;
+      *reinterpret_cast<u32x4_t*>(k_wr + (arena + own) * kDK + j * 8) = kx;
       if (j == 0) {
         beamKq[bb] = kq;
-        a.rec_alpha[arena + own] = beamAl[bb];
+        al_wr[arena + own] = beamAl[bb];
       }
+    }
+    // this wave's 32 rows of S_ctx, bf16 high and low halves, resident for the rest of the tile;
+    // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16
+    {
+      const int W = d_v / 32;
+      const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
+      const u32x4_t* __restrict__ fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+            sf[ks][mi][hl] = __builtin_bit_cast(
+                bf16x8_t, fr[hl * half + (((size_t)wave * kKS + ks) * 2 + mi) * 64 + lane]);
     }
   }
   __syncthreads();
 
   // ---- phase 2: MFMA contraction + replay + append, 16 beams per iteration ----
-  const int gq = lane >> 4, col = lane & 15;
-  const int dvi = wave * 32 + 2 * col;  // this lane's two d_v elements
   for (int mt = 0; mt * 16 < nb; ++mt) {
+    const int bb = mt * 16 + col;  // this lane's beam
     floatx4_t pk[2], pq[2];
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      pk[nn] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      pq[nn] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < 2; ++mi) {
+      pk[mi] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      pq[mi] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
     }
-    const int arow = mt * 16 + col;  // A operand: lane l holds row l%16, k = 8 (l/16) .. +7
+    // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const bf16x8_t ak =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + arow * kXRow + ks * 64 + gq * 16));
-      const bf16x8_t aq = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + arow) * kXRow + ks * 64 + gq * 16));
+      const bf16x8_t bk =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
+      const bf16x8_t bq = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn) {
+      for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl) {
-          pk[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sf[ks][nn][hl], pk[nn], 0, 0, 0);
-          pq[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sf[ks][nn][hl], pq[nn], 0, 0, 0);
+          pk[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][mi][hl], bk, pk[mi], 0, 0, 0);
+          pq[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][mi][hl], bq, pq[mi], 0, 0, 0);
         }
       }
     }
+    const int bc = min(bb, nb - 1);
+    const float A = beamA[bc];
+    float p[2][4], sq[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bb = mt * 16 + 4 * gq + i;
-      if (bb >= nb) continue;
-      const float A = beamA[bb];
-      float p0 = A * pk[0][i], p1 = A * pk[1][i];
-      float s0 = A * pq[0][i], s1 = A * pq[1][i];
-      for (int m0 = 0; m0 < nch; m0 += 4) {
-        f32x2_t U[4];
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int m = m0 + u < nch ? m0 + u : nch - 1;
-          U[u] = *reinterpret_cast<const f32x2_t*>(a.rec_u + (arena + slot_tab[bb * L + m]) * d_v + dvi);
-        }
+      for (int e = 0; e < 4; ++e) {
+        p[mi][e] = A * pk[mi][e];
+        sq[mi][e] = A * pq[mi][e];
+      }
+    const f32x2_t vv[2] = {V[0], V[1]};
+    for (int m0 = 0; m0 < nch; m0 += kChunk) {
+      if (m0 > 0) gather(mt, m0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (m0 + u < nch) {
-            const float ck = coefk[bb * L + m0 + u], cq = coefq[bb * L + m0 + u];
-            p0 += ck * U[u].x;
-            p1 += ck * U[u].y;
-            s0 += cq * U[u].x;
-            s1 += cq * U[u].y;
-          }
+      for (int u = 0; u < kChunk; ++u) {
+        if (m0 + u < nch) {
+          const f32x2_t c = coef[bc * L + m0 + u];
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              p[mi][e] += c.x * U[u][mi][e];
+              sq[mi][e] += c.y * U[u][mi][e];
+            }
         }
       }
-      const size_t row = in_row(bb);
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vin + row * d_v + dvi);
+    }
+    if ((mt + 1) * 16 < nb) gather(mt + 1, 0);  // next tile's loads fly during these stores and its MFMAs
+    if (bb < nb) {
       const float al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
-      f32x2_t u2, o2;
-      u2.x = be * (bf16_bits_to_f32(vv & 0xFFFFu) - al * p0);
-      u2.y = be * (bf16_bits_to_f32(vv >> 16) - al * p1);
-      o2.x = al * s0 + kq * u2.x;
-      o2.y = al * s1 + kq * u2.y;
-      const int own = (a.t - 1) * a.B_max + b0 + bb;
-      *reinterpret_cast<f32x2_t*>(a.rec_u + (arena + own) * d_v + dvi) = u2;
-      *reinterpret_cast<f32x2_t*>(a.o + row * d_v + dvi) = o2;
+      const int own = nch * a.B_max + b0 + bb;
+      float* ur = u_wr + (arena + own) * d_v + dv0;
+      float* orow = o_wr + in_row(bb) * d_v + dv0;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const uint32_t w0 = __float_as_uint(vv[mi].x), w1 = __float_as_uint(vv[mi].y);
+        const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
+                             bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
+        f32x4_t u4, o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float uu = be * (v4[e] - al * p[mi][e]);
+          u4[e] = uu;
+          o4[e] = al * sq[mi][e] + kq * uu;
+        }
+        *reinterpret_cast<f32x4_t*>(ur + 16 * mi) = u4;
+        *reinterpret_cast<f32x4_t*>(orow + 16 * mi) = o4;
+      }
     }
   }
 }
 
 bool fused_supported(int d_k, int d_v, int L_max) {
-  return d_k == kDK && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && fused_lds_bytes(16, L_max) <= 160 * 1024;
+  return d_k == kDK && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && fused_lds_bytes(16, L_max, d_v) <= 160 * 1024;
 }
 
-size_t fused_lds_bytes(int tile, int L_max) { return (size_t)fused_layout(tile, L_max).total; }
+size_t fused_lds_bytes(int tile, int L_max, int d_v) {
+  (void)d_v;
+  return (size_t)fused_layout(tile, L_max).total;
+}
 
 int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
-  (void)d_v;
   if (requested) return requested;
   const long G = (long)R * H;
   const int cands[3] = {64, 32, 16};
   for (int c : cands) {
     const long wgs = G * ((n + c - 1) / c);
-    if (wgs >= 1024 && fused_lds_bytes(c, L_max) <= 64 * 1024) return c;
+    if (wgs >= 1024 && fused_lds_bytes(c, L_max, d_v) <= 64 * 1024) return c;
   }
   return 16;
 }
@@ -291,7 +363,7 @@ int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
 hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s) {
   const int ntile = (a.n + tile - 1) / tile;
   dim3 grid((unsigned)((size_t)a.R * a.H * ntile)), block(2 * a.d_v);
-  const size_t lds = fused_lds_bytes(tile, a.L_max);
+  const size_t lds = fused_lds_bytes(tile, a.L_max, a.d_v);
 #define ONELA_FUSED_CASE(NB)                                                                                   \
   case NB:                                                                                                     \
     if (lds > 64 * 1024) {                                                                                     \

@@ -45,6 +45,7 @@ def expected_bytes(c):
     fused = (c.mode == onela.ONELA_MODE_REPLAY and c.qkv_dtype == onela.ONELA_BF16 and not c.flags
              and dk == 128 and dv % 32 == 0)
     total = 256 + up(R * H * dk * dv * 4) + up(R * H * dk * dv * 4 if fused else 0) + up(L * R * B * L * 4)
+    total += up(2 * R * H * B * (L + 1) * 4 if fused else 0)
     if c.mode == onela.ONELA_MODE_REPLAY:
         slots = B * L
         total += up(R * H * slots * dk * s_in) + up(R * H * slots * dv * 4) + up(R * H * slots * 4)
