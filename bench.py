@@ -11,6 +11,7 @@ Prints one JSON line.  Extra objects:
                 the run's own chain tables) / its average launch time from HIP events in the timed region
   cpu_baseline  the float64 CPU oracle (record-replay form) timed on whole requests of the same workload
   fullstate     the controlled FullState path (dense per-beam state) on the same inputs
+  hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
 """
 
 from __future__ import annotations
@@ -70,6 +71,31 @@ def algorithmic_bytes(cfg, chains, parents):
         nbytes += anc * H * rec                           # distinct ancestor records read
         out.append(nbytes)
     return out
+
+
+def hbm_probe(torch, dev, gib: float = 2.0):
+    """Achievable HBM bandwidth with plain torch kernels on this GPU: copy (1 read + 1 write) and fill (write
+    only), best of 5.  Context for the roofline fraction; not part of the timed decode."""
+    n = int(gib * (1 << 30)) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+
+    def best(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        out = 0.0
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out = max(out, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        return out
+
+    res = {"copy_GBs": best(lambda: y.copy_(x), 8.0 * n), "fill_GBs": best(lambda: y.fill_(2.0), 4.0 * n)}
+    del x, y
+    return res
 
 
 def cpu_baseline(cfg, steps, budget_s: float):
@@ -252,6 +278,7 @@ def main():
                      "mfma_frac": mfma_flops / (kernel_ms.sum(axis=1).mean() * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
         "context_ms": context_ms,
     }
+    line["hbm_probe"] = hbm_probe(torch, dev)
     sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
     del view
     ctx.close()

@@ -85,6 +85,10 @@ onela_status check_config(const onela_config* c) {
   if (slots_total > 9.0e15) return fail(ONELA_ERR_INVALID_ARG, "configuration too large");
   if ((double)c->num_requests * c->max_beams * c->num_heads > 2.0e9)
     return fail(ONELA_ERR_INVALID_ARG, "num_requests * max_beams * num_heads exceeds the launch grid");
+  // per-(request, head) record arenas and per-request step inputs are addressed with 32-bit offsets
+  if ((double)c->max_beams * c->max_steps * (c->d_k > c->d_v ? c->d_k : c->d_v) * 4.0 >= 2147483648.0 ||
+      (double)c->max_beams * c->num_heads * (c->d_k > c->d_v ? c->d_k : c->d_v) * 4.0 >= 2147483648.0)
+    return fail(ONELA_ERR_INVALID_ARG, "max_beams * max_steps * d or max_beams * num_heads * d exceeds 2^31 bytes");
   return ONELA_OK;
 }
 

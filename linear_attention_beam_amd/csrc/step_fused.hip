@@ -34,16 +34,21 @@ constexpr int kItems = 16;           // chain keys in flight per 16-lane group (
 constexpr int kChunk = 3;            // chain records in flight per beam (phase 2)
 
 struct FusedLds {
-  int xs, slot, alph, coef, beamA, beamAl, beamBe, beamKq, beamPar, total;  // alph: c_j
+  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, total;
 };
 
+// Per-beam tables use an odd row stride so that 16 beams read by one wave fall in distinct LDS banks.
+__host__ __device__ inline int table_stride(int L) { return L | 1; }
+
 __host__ __device__ inline FusedLds fused_layout(int NB, int L) {
+  const int LS = table_stride(L);
   FusedLds l;
   int off = 0;
   l.xs = off;      off += 2 * NB * kXRow;  // k rows, then q rows
-  l.slot = off;    off += NB * L * 4;
-  l.alph = off;    off += NB * L * 4;      // c_j
-  l.coef = off;    off += NB * L * 8;      // (c_j (K_j . k), c_j (K_j . q)) pairs
+  l.slot = off;    off += NB * LS * 4;     // chain slots
+  l.alph = off;    off += NB * LS * 4;     // c_j
+  l.coef = off;    off += NB * LS * 8;     // (c_j (K_j . k), c_j (K_j . q)) pairs
+  l.item = off;    off += NB * L * 8;      // phase-1 work list: (slot, bb << 16 | bb * LS + m)
   l.beamA = off;   off += NB * 4;
   l.beamAl = off;  off += NB * 4;
   l.beamBe = off;  off += NB * 4;
@@ -58,11 +63,13 @@ template <int NB>
 __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
+  const int LS = table_stride(L);
   const FusedLds lay = fused_layout(NB, L);
   unsigned char* xs = lds + lay.xs;
   int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
   float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
   f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
+  int2* item_tab = reinterpret_cast<int2*>(lds + lay.item);
   float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
   float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
   float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
@@ -88,18 +95,21 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   const int nb = min(NB, n - b0);
   const int nch = a.t - 1;
   const size_t arena = (size_t)rh * a.slots;
-  const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v);
+  // Uniform per-workgroup bases; per-lane offsets are 32-bit (the host checks that they fit).
+  const size_t row0 = ((size_t)r * n + b0) * H + h;  // input row of beam b0 at this head
+  const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q) + row0 * kDK;
+  const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k) + row0 * kDK;
+  const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v) + row0 * d_v;
+  float* __restrict__ o_wr = a.o + row0 * d_v;
+  const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs
   // Records are read only at slots of earlier steps and written only at this step's slots, so the read
   // and write views never touch the same element.
-  const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k);
-  uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k);
-  const float* __restrict__ u_rd = a.rec_u;
-  float* __restrict__ u_wr = a.rec_u;
-  float* __restrict__ al_wr = a.rec_alpha;
-  float* __restrict__ o_wr = a.o;
-  auto in_row = [&](int bb) { return ((size_t)r * n + b0 + bb) * H + h; };
+  const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
+  uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k) + arena * kDK;
+  const float* __restrict__ u_rd = a.rec_u + arena * d_v;
+  float* __restrict__ u_wr = a.rec_u + arena * d_v;
+  float* __restrict__ al_wr = a.rec_alpha + arena;
+  auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
 
   // ---- phase 0: parents; stage k and q; chains and their alphas; per-beam alpha and beta ----
   for (int bb = tid; bb < NB; bb += nthreads) {
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     const int row = idx >> 4, c = idx & 15;  // row < NB: key rows, row >= NB: query rows
     const int bb = row < NB ? row : row - NB;
     u32x4_t val = {0u, 0u, 0u, 0u};
-    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + in_row(bb) * kDK + c * 8);
+    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)bb * hk + c * 8);
     *reinterpret_cast<u32x4_t*>(xs + row * kXRow + c * 16) = val;
   }
   __syncthreads();
@@ -144,8 +154,10 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
       const int idx = base + u * nthreads + tid;
       if (idx < nb * nch) {
         const int bb = idx / nch, m = idx - bb * nch;
-        slot_tab[bb * L + m] = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
-        c_tab[bb * L + m] = dec[u];
+        const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
+        slot_tab[bb * LS + m] = sl;
+        c_tab[bb * LS + m] = dec[u];
+        item_tab[idx] = make_int2(sl, (bb << 16) | (bb * LS + m));
         a.decay_out[((size_t)rh * a.B_max + b0 + bb) * drow + m] = dec[u] * beamAl[bb];
         if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
       }
@@ -173,27 +185,29 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   }
   __syncthreads();
 
-  // ---- phase 2 gathers: for this lane's beam (col) in beam tile mt, records m0 .. m0+kChunk-1 of its
-  // chain: u at its two 4-row pieces; v at the same rows when m0 == 0.  The first tile's gathers fly
-  // during phase 1.
+  // ---- phase 2 gathers.  v of this lane's beam in every beam tile is loaded here, with the first round
+  // trip; the chain records' u (kChunk at a time, its two 4-row pieces) is gathered per beam tile, the
+  // first tile's during phase 1 and each next tile's during the current tile's stores and MFMAs.
   const int gq = lane >> 4, col = lane & 15;
   const int dv0 = wave * 32 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3 and dv0+16 .. dv0+19
+  constexpr int kTiles = NB / 16;
+  f32x2_t V[kTiles][2];
+#pragma unroll
+  for (int mt = 0; mt < kTiles; ++mt) {
+    const unsigned vo = (unsigned)min(mt * 16 + col, nb - 1) * hv + dv0;
+    V[mt][0] = *reinterpret_cast<const f32x2_t*>(vin + vo);
+    V[mt][1] = *reinterpret_cast<const f32x2_t*>(vin + vo + 16);
+  }
   f32x4_t U[kChunk][2];
-  f32x2_t V[2];
   auto gather = [&](int mt, int m0) {
     const int bb = min(mt * 16 + col, nb - 1);
-    if (m0 == 0) {
-      const uint16_t* vr = vin + in_row(bb) * d_v + dv0;
-      V[0] = *reinterpret_cast<const f32x2_t*>(vr);
-      V[1] = *reinterpret_cast<const f32x2_t*>(vr + 16);
-    }
     if (nch > 0) {
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const int m = min(m0 + u, nch - 1);
-        const float* ur = u_rd + (arena + slot_tab[bb * L + m]) * d_v + dv0;
-        U[u][0] = *reinterpret_cast<const f32x4_t*>(ur);
-        U[u][1] = *reinterpret_cast<const f32x4_t*>(ur + 16);
+        const unsigned uo = (unsigned)slot_tab[bb * LS + m] * d_v + dv0;
+        U[u][0] = *reinterpret_cast<const f32x4_t*>(u_rd + uo);
+        U[u][1] = *reinterpret_cast<const f32x4_t*>(u_rd + uo + 16);
       }
     }
   };
@@ -206,43 +220,37 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     const int ngroups = nthreads >> 4;
     const int items = nb * nch;
     for (int it0 = g * kItems; it0 < items; it0 += ngroups * kItems) {
-      const int bb0 = it0 / nch, m00 = it0 - bb0 * nch;
       u32x4_t K[kItems];
-      {
-        int bb = bb0, m = m00;
+      int2 it[kItems];
 #pragma unroll
-        for (int u = 0; u < kItems; ++u) {
-          const bool valid = it0 + u < items;
-          const int s = slot_tab[(valid ? bb : bb0) * L + (valid ? m : m00)];
-          K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + (arena + s) * kDK + j * 8);
-          if (++m == nch) { m = 0; ++bb; }
-        }
+      for (int u = 0; u < kItems; ++u) {
+        it[u] = item_tab[min(it0 + u, items - 1)];
+        K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)it[u].x * kDK + j * 8));
       }
-      int bb = bb0, m = m00;
 #pragma unroll
       for (int u = 0; u < kItems; ++u) {
         if (it0 + u < items) {  // uniform over the 16 lanes of the group
+          const int pos = it[u].y & 0xFFFF, bb = it[u].y >> 16;
           const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
           const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
           const float dk = row16_sum(dot8_bf16(K[u], kx));
           const float dq = row16_sum(dot8_bf16(K[u], qx));
           if (j == 0) {
-            const float c = c_tab[bb * L + m];
-            coef[bb * L + m] = (f32x2_t){c * dk, c * dq};
+            const float c = c_tab[pos];
+            coef[pos] = (f32x2_t){c * dk, c * dq};
           }
         }
-        if (++m == nch) { m = 0; ++bb; }
       }
     }
     for (int bb = g; bb < nb; bb += ngroups) {
       const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
       const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
       const float kq = row16_sum(dot8_bf16(kx, qx));
-      const int own = nch * a.B_max + b0 + bb;
-      *reinterpret_cast<u32x4_t*>(k_wr + (arena + own) * kDK + j * 8) = kx;
+      const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
+      *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j * 8)) = kx;
       if (j == 0) {
         beamKq[bb] = kq;
-        al_wr[arena + own] = beamAl[bb];
+        al_wr[own] = beamAl[bb];
       }
     }
     // this wave's 32 rows of S_ctx, bf16 high and low halves, resident for the rest of the tile;
@@ -264,7 +272,9 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   __syncthreads();
 
   // ---- phase 2: MFMA contraction + replay + append, 16 beams per iteration ----
-  for (int mt = 0; mt * 16 < nb; ++mt) {
+#pragma unroll
+  for (int mt = 0; mt < kTiles; ++mt) {
+    if (mt * 16 >= nb) break;
     const int bb = mt * 16 + col;  // this lane's beam
     floatx4_t pk[2], pq[2];
 #pragma unroll
@@ -298,13 +308,13 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
         p[mi][e] = A * pk[mi][e];
         sq[mi][e] = A * pq[mi][e];
       }
-    const f32x2_t vv[2] = {V[0], V[1]};
+    const f32x2_t vv[2] = {V[mt][0], V[mt][1]};
     for (int m0 = 0; m0 < nch; m0 += kChunk) {
       if (m0 > 0) gather(mt, m0);
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         if (m0 + u < nch) {
-          const f32x2_t c = coef[bc * L + m0 + u];
+          const f32x2_t c = coef[bc * LS + m0 + u];
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -318,9 +328,9 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     if ((mt + 1) * 16 < nb) gather(mt + 1, 0);  // next tile's loads fly during these stores and its MFMAs
     if (bb < nb) {
       const float al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
-      const int own = nch * a.B_max + b0 + bb;
-      float* ur = u_wr + (arena + own) * d_v + dv0;
-      float* orow = o_wr + in_row(bb) * d_v + dv0;
+      const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
+      float* ur = u_wr + (own * d_v + dv0);
+      float* orow = o_wr + ((unsigned)bb * hv + dv0);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const uint32_t w0 = __float_as_uint(vv[mi].x), w1 = __float_as_uint(vv[mi].y);
