@@ -2,7 +2,7 @@
 // state, record replay and record append in one kernel ("Scientific Impact Assessment: OneLA", §1: a fused
 // GPU kernel reuses S_ctx across beams; paper index page, Abstract).
 //
-// Workgroup = (request, head, tile of NB beams); d_v / 32 waves of 64 lanes (d_k = 128 fixed).
+// Workgroup = (request, head, tile of NB beams); d_v / 16 waves of 64 lanes (d_k = 128 fixed).
 //   Phase 0  ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each beam's chain is its
 //            parent's chain from the previous table plus its own slot; the head-0 workgroups write the new
 //            table.  The decays along a chain (A = prod alpha, c_j = prod of the alphas after record j) are
@@ -11,12 +11,12 @@
 //            step, so no record alpha is gathered.  Stage k and q of the tile in LDS.
 //   Phase 1  (16 lanes per beam) dot products of the chain keys with k and q, and k . q, reduced with DPP
 //            inside a 16-lane row; append the record key and alpha.
-//   Phase 2  wave w owns d_v rows 32w .. 32w+31 of S_ctx, whose bf16 high and low halves stay in registers
+//   Phase 2  wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay in registers
 //            for the whole tile (each S_ctx element is read once per tile and reused by all NB beams).
 //            For 16 beams at a time, v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over
 //            d_k, high then low half into one float32 accumulator.  In the accumulator lane l holds beam
-//            l % 16 and d_v rows 4 (l / 16) .. +3 of each 16-row block, so the replay works per beam on
-//            16-byte pieces: two float4 loads of each chain record's u, float4 stores of u and o:
+//            l % 16 and d_v rows 4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on
+//            16-byte pieces: one float4 load of each chain record's u, float4 stores of u and o:
 //              p = A P_k + sum_j c_j (K_j.k) U_j,  u = beta (v - alpha p),
 //              o = alpha (A P_q + sum_j c_j (K_j.q) U_j) + (k.q) u.
 // Workgroups of one (request, head) are mapped to the same XCD (dispatch is round-robin over the 8 XCDs)
@@ -30,8 +30,8 @@ namespace {
 constexpr int kDK = 128;             // d_k of the fused kernel
 constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
-constexpr int kItems = 16;           // chain keys in flight per 16-lane group (phase 1)
-constexpr int kChunk = 3;            // chain records in flight per beam (phase 2)
+constexpr int kItems = 4;            // chain keys in flight per 16-lane group (phase 1)
+constexpr int kChunk = 4;            // chain records in flight per beam (phase 2)
 
 struct FusedLds {
   int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, total;
@@ -60,7 +60,7 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L) {
 }  // namespace
 
 template <int NB>
-__global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) {
+__global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
   const int LS = table_stride(L);
@@ -186,35 +186,35 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   __syncthreads();
 
   // ---- phase 2 gathers.  v of this lane's beam in every beam tile is loaded here, with the first round
-  // trip; the chain records' u (kChunk at a time, its two 4-row pieces) is gathered per beam tile, the
-  // first tile's during phase 1 and each next tile's during the current tile's stores and MFMAs.
+  // trip; the chain records' u (kChunk at a time, this lane's 4-row piece) is gathered per beam tile, the
+  // first tile's during phase 1 and each next tile's during the current tile's stores and MFMAs.  Only
+  // records that exist are loaded, so a short chain issues no redundant requests.
   const int gq = lane >> 4, col = lane & 15;
-  const int dv0 = wave * 32 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3 and dv0+16 .. dv0+19
+  const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
   constexpr int kTiles = NB / 16;
-  f32x2_t V[kTiles][2];
+  f32x2_t V[kTiles];
 #pragma unroll
   for (int mt = 0; mt < kTiles; ++mt) {
     const unsigned vo = (unsigned)min(mt * 16 + col, nb - 1) * hv + dv0;
-    V[mt][0] = *reinterpret_cast<const f32x2_t*>(vin + vo);
-    V[mt][1] = *reinterpret_cast<const f32x2_t*>(vin + vo + 16);
+    V[mt] = *reinterpret_cast<const f32x2_t*>(vin + vo);
   }
-  f32x4_t U[kChunk][2];
+  f32x4_t U[kChunk];
   auto gather = [&](int mt, int m0) {
     const int bb = min(mt * 16 + col, nb - 1);
     if (nch > 0) {
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        const int m = min(m0 + u, nch - 1);
-        const unsigned uo = (unsigned)slot_tab[bb * LS + m] * d_v + dv0;
-        U[u][0] = *reinterpret_cast<const f32x4_t*>(u_rd + uo);
-        U[u][1] = *reinterpret_cast<const f32x4_t*>(u_rd + uo + 16);
+        if (m0 + u < nch) {
+          const unsigned uo = (unsigned)slot_tab[bb * LS + m0 + u] * d_v + dv0;
+          U[u] = *reinterpret_cast<const f32x4_t*>(u_rd + uo);
+        }
       }
     }
   };
   gather(0, 0);
 
   // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q; then k . q; append k, alpha ----
-  bf16x8_t sf[kKS][2][2];
+  bf16x8_t sf[kKS][2];
   {
     const int g = tid >> 4, j = tid & 15;
     const int ngroups = nthreads >> 4;
@@ -224,8 +224,10 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
       int2 it[kItems];
 #pragma unroll
       for (int u = 0; u < kItems; ++u) {
-        it[u] = item_tab[min(it0 + u, items - 1)];
-        K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)it[u].x * kDK + j * 8));
+        if (it0 + u < items) {
+          it[u] = item_tab[it0 + u];
+          K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)it[u].x * kDK + j * 8));
+        }
       }
 #pragma unroll
       for (int u = 0; u < kItems; ++u) {
@@ -253,8 +255,9 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
         al_wr[own] = beamAl[bb];
       }
     }
-    // this wave's 32 rows of S_ctx, bf16 high and low halves, resident for the rest of the tile;
-    // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16
+    // this wave's 16 rows of S_ctx, bf16 high and low halves, resident for the rest of the tile;
+    // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16, and
+    // wave x takes the block w = x / 2, mi = x % 2
     {
       const int W = d_v / 32;
       const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
@@ -262,11 +265,9 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-            sf[ks][mi][hl] = __builtin_bit_cast(
-                bf16x8_t, fr[hl * half + (((size_t)wave * kKS + ks) * 2 + mi) * 64 + lane]);
+        for (int hl = 0; hl < 2; ++hl)
+          sf[ks][hl] = __builtin_bit_cast(
+              bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
     }
   }
   __syncthreads();
@@ -276,12 +277,7 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
   for (int mt = 0; mt < kTiles; ++mt) {
     if (mt * 16 >= nb) break;
     const int bb = mt * 16 + col;  // this lane's beam
-    floatx4_t pk[2], pq[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      pk[mi] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      pq[mi] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-    }
+    floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
     // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
@@ -290,25 +286,20 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
       const bf16x8_t bq = __builtin_bit_cast(
           bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          pk[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][mi][hl], bk, pk[mi], 0, 0, 0);
-          pq[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][mi][hl], bq, pq[mi], 0, 0, 0);
-        }
+      for (int hl = 0; hl < 2; ++hl) {
+        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
+        pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
       }
     }
     const int bc = min(bb, nb - 1);
     const float A = beamA[bc];
-    float p[2][4], sq[2][4];
+    float p[4], sq[4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[mi][e] = A * pk[mi][e];
-        sq[mi][e] = A * pq[mi][e];
-      }
-    const f32x2_t vv[2] = {V[mt][0], V[mt][1]};
+    for (int e = 0; e < 4; ++e) {
+      p[e] = A * pk[e];
+      sq[e] = A * pq[e];
+    }
+    const f32x2_t vv = V[mt];
     for (int m0 = 0; m0 < nch; m0 += kChunk) {
       if (m0 > 0) gather(mt, m0);
 #pragma unroll
@@ -316,12 +307,10 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
         if (m0 + u < nch) {
           const f32x2_t c = coef[bc * LS + m0 + u];
 #pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              p[mi][e] += c.x * U[u][mi][e];
-              sq[mi][e] += c.y * U[u][mi][e];
-            }
+          for (int e = 0; e < 4; ++e) {
+            p[e] += c.x * U[u][e];
+            sq[e] += c.y * U[u][e];
+          }
         }
       }
     }
@@ -329,23 +318,18 @@ __global__ __launch_bounds__(512) void step_fused_kernel(StepArgs a, int ntile) 
     if (bb < nb) {
       const float al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
       const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-      float* ur = u_wr + (own * d_v + dv0);
-      float* orow = o_wr + ((unsigned)bb * hv + dv0);
+      const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
+      const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
+                           bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
+      f32x4_t u4, o4;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const uint32_t w0 = __float_as_uint(vv[mi].x), w1 = __float_as_uint(vv[mi].y);
-        const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
-                             bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
-        f32x4_t u4, o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float uu = be * (v4[e] - al * p[mi][e]);
-          u4[e] = uu;
-          o4[e] = al * sq[mi][e] + kq * uu;
-        }
-        *reinterpret_cast<f32x4_t*>(ur + 16 * mi) = u4;
-        *reinterpret_cast<f32x4_t*>(orow + 16 * mi) = o4;
+      for (int e = 0; e < 4; ++e) {
+        const float uu = be * (v4[e] - al * p[e]);
+        u4[e] = uu;
+        o4[e] = al * sq[e] + kq * uu;
       }
+      *reinterpret_cast<f32x4_t*>(u_wr + (own * d_v + dv0)) = u4;
+      *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
     }
   }
 }
@@ -372,7 +356,7 @@ int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
 
 hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s) {
   const int ntile = (a.n + tile - 1) / tile;
-  dim3 grid((unsigned)((size_t)a.R * a.H * ntile)), block(2 * a.d_v);
+  dim3 grid((unsigned)((size_t)a.R * a.H * ntile)), block(4 * a.d_v);
   const size_t lds = fused_lds_bytes(tile, a.L_max, a.d_v);
 #define ONELA_FUSED_CASE(NB)                                                                                   \
   case NB:                                                                                                     \
