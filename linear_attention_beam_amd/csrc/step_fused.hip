@@ -3,17 +3,20 @@
 // GPU kernel reuses S_ctx across beams; paper index page, Abstract).
 //
 // Workgroup = (request, head, tile of NB beams); d_v / 16 waves of 64 lanes (d_k = 128 fixed).
-//   Phase 0  ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each beam's chain is its
-//            parent's chain from the previous table plus its own slot; the head-0 workgroups write the new
-//            table.  The decays along a chain (A = prod alpha, c_j = prod of the alphas after record j) are
-//            kept per (request, head, beam) next to the index: a beam reads its parent's row, and writes
-//            its own (c_j alpha_b for the parent's records, 1 for its own record, A alpha_b) for the next
-//            step, so no record alpha is gathered.  Stage k and q of the tile in LDS.
-//   Phase 1  (16 lanes per beam) dot products of the chain keys with k and q, and k . q, reduced with DPP
-//            inside a 16-lane row; append the record key and alpha.
-//   Phase 2  wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay in registers
-//            for the whole tile (each S_ctx element is read once per tile and reused by all NB beams).
-//            For 16 beams at a time, v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over
+//   Phase 0  everything that needs nothing from the ancestry goes out in the first round trip: parents,
+//            alpha and beta; k, q and v rows of the tile, staged in LDS with 16-byte loads; this wave's
+//            S_ctx rows.  Wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay
+//            in registers for the whole tile (each S_ctx element is read once per tile and reused by all
+//            NB beams).  Then the ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each
+//            beam's chain is its parent's chain from the previous table plus its own slot; the head-0
+//            workgroups write the new table.  The decays along a chain (A = prod alpha, c_j = prod of the
+//            alphas after record j) are kept per (request, head, beam) next to the index: a beam reads its
+//            parent's row (chain entries and A in one round trip), and writes its own (c_j alpha_b for the
+//            parent's records, 1 for its own record, A alpha_b) for the next step, so no record alpha is
+//            gathered.
+//   Phase 1  (16 lanes per (beam, chain record)) dot products of the chain keys with k and q, and k . q,
+//            reduced with DPP inside a 16-lane row; append the record key and alpha.
+//   Phase 2  for 16 beams at a time, v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over
 //            d_k, high then low half into one float32 accumulator.  In the accumulator lane l holds beam
 //            l % 16 and d_v rows 4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on
 //            16-byte pieces: one float4 load of each chain record's u, float4 stores of u and o:
@@ -34,13 +37,13 @@ constexpr int kItems = 4;            // chain keys in flight per 16-lane group (
 constexpr int kChunk = 4;            // chain records in flight per beam (phase 2)
 
 struct FusedLds {
-  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, total;
+  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, vs, vrow, total;
 };
 
 // Per-beam tables use an odd row stride so that 16 beams read by one wave fall in distinct LDS banks.
 __host__ __device__ inline int table_stride(int L) { return L | 1; }
 
-__host__ __device__ inline FusedLds fused_layout(int NB, int L) {
+__host__ __device__ inline FusedLds fused_layout(int NB, int L, int d_v) {
   const int LS = table_stride(L);
   FusedLds l;
   int off = 0;
@@ -54,9 +57,14 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L) {
   l.beamBe = off;  off += NB * 4;
   l.beamKq = off;  off += NB * 4;
   l.beamPar = off; off += NB * 4;
+  l.vrow = d_v * 2 + 16;
+  l.vs = off;      off += NB * l.vrow;     // v rows (bf16, padded like the k and q rows)
   l.total = off;
   return l;
 }
+// LDS a workgroup may take without LDS cutting the VGPR-limited occupancy (4 waves per SIMD, 16 per CU):
+// 160 KB per CU shared by 16 / (d_v / 16) workgroups.
+inline size_t lds_budget(int d_v) { return (size_t)640 * d_v; }
 }  // namespace
 
 template <int NB>
@@ -64,8 +72,9 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
   const int LS = table_stride(L);
-  const FusedLds lay = fused_layout(NB, L);
+  const FusedLds lay = fused_layout(NB, L, d_v);
   unsigned char* xs = lds + lay.xs;
+  unsigned char* vs = lds + lay.vs;
   int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
   float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
   f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   float* __restrict__ al_wr = a.rec_alpha + arena;
   auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
 
-  // ---- phase 0: parents; stage k and q; chains and their alphas; per-beam alpha and beta ----
+  // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers ----
   for (int bb = tid; bb < NB; bb += nthreads) {
     const bool live = bb < nb;
     int p = 0;
@@ -133,46 +142,77 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
     if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)bb * hk + c * 8);
     *reinterpret_cast<u32x4_t*>(xs + row * kXRow + c * 16) = val;
   }
+  {
+    const int vc = d_v >> 3;  // 16-byte pieces per v row
+    for (int idx = tid; idx < NB * vc; idx += nthreads) {
+      const int bb = idx / vc, c = idx - bb * vc;
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (bb < nb) val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)bb * hv + c * 8);
+      *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + c * 16) = val;
+    }
+  }
+  const int gq = lane >> 4, col = lane & 15;
+  const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
+  constexpr int kTiles = NB / 16;
+  // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16; wave x
+  // takes the block w = x / 2, mi = x % 2
+  bf16x8_t sf[kKS][2];
+  {
+    const int W = d_v / 32;
+    const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
+    const u32x4_t* __restrict__ fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        sf[ks][hl] = __builtin_bit_cast(
+            bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
+  }
   __syncthreads();
-  const int drow = L + 1;  // decay row: c_0 .. c_{L-1}, then A
-  for (int base = 0; base < nb * nch; base += 4 * nthreads) {
+
+  // ---- phase 0 (cont.): the parents' chain rows and decay rows in one round trip; this step's rows ----
+  const int drow = L + 1;    // decay row: c_0 .. c_{L-1}, then A
+  const int nper = nch + 1;  // per beam: nch chain entries, then the parent's total decay A
+  for (int base = 0; base < nb * nper; base += 4 * nthreads) {
     int raw[4];
     float dec[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + u * nthreads + tid;
       raw[u] = 0;
-      dec[u] = 0.f;
-      if (idx < nb * nch) {
-        const int bb = idx / nch, m = idx - bb * nch;
-        raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
-        dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
+      dec[u] = 1.f;
+      if (idx < nb * nper) {
+        const int bb = idx / nper, m = idx - bb * nper;
+        if (m < nch) {
+          raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
+          dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
+        } else if (nch > 0) {
+          dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L];
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + u * nthreads + tid;
-      if (idx < nb * nch) {
-        const int bb = idx / nch, m = idx - bb * nch;
-        const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
-        slot_tab[bb * LS + m] = sl;
-        c_tab[bb * LS + m] = dec[u];
-        item_tab[idx] = make_int2(sl, (bb << 16) | (bb * LS + m));
-        a.decay_out[((size_t)rh * a.B_max + b0 + bb) * drow + m] = dec[u] * beamAl[bb];
-        if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
+      if (idx < nb * nper) {
+        const int bb = idx / nper, m = idx - bb * nper;
+        float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
+        if (m < nch) {
+          const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
+          slot_tab[bb * LS + m] = sl;
+          c_tab[bb * LS + m] = dec[u];
+          item_tab[bb * nch + m] = make_int2(sl, (bb << 16) | (bb * LS + m));
+          dout[m] = dec[u] * beamAl[bb];
+          if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
+        } else {
+          dout[nch] = 1.f;
+          dout[L] = dec[u] * beamAl[bb];
+          beamA[bb] = dec[u];
+        }
       }
     }
   }
-  for (int bb = tid; bb < NB; bb += nthreads) {
-    float A = 0.f;
-    if (bb < nb) {
-      A = nch > 0 ? a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L] : 1.f;
-      float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
-      dout[nch] = 1.f;
-      dout[L] = A * beamAl[bb];
-    }
-    beamA[bb] = A;
-  }
+  for (int bb = nb + tid; bb < NB; bb += nthreads) beamA[bb] = 0.f;
   if (h == 0) {  // the rest of each row: own slot, then -1; rows of beams >= n are all -1
     for (int idx = tid; idx < nb * (L - nch); idx += nthreads) {
       const int bb = idx / (L - nch), m = nch + idx - bb * (L - nch);
@@ -185,19 +225,9 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   }
   __syncthreads();
 
-  // ---- phase 2 gathers.  v of this lane's beam in every beam tile is loaded here, with the first round
-  // trip; the chain records' u (kChunk at a time, this lane's 4-row piece) is gathered per beam tile, the
-  // first tile's during phase 1 and each next tile's during the current tile's stores and MFMAs.  Only
-  // records that exist are loaded, so a short chain issues no redundant requests.
-  const int gq = lane >> 4, col = lane & 15;
-  const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
-  constexpr int kTiles = NB / 16;
-  f32x2_t V[kTiles];
-#pragma unroll
-  for (int mt = 0; mt < kTiles; ++mt) {
-    const unsigned vo = (unsigned)min(mt * 16 + col, nb - 1) * hv + dv0;
-    V[mt] = *reinterpret_cast<const f32x2_t*>(vin + vo);
-  }
+  // ---- phase 2 gathers.  The chain records' u (kChunk at a time, this lane's 4-row piece) is gathered per
+  // beam tile, the first tile's during phase 1 and each next tile's during the current tile's stores and
+  // MFMAs.  Only records that exist are loaded, so a short chain issues no redundant requests.
   f32x4_t U[kChunk];
   auto gather = [&](int mt, int m0) {
     const int bb = min(mt * 16 + col, nb - 1);
@@ -214,7 +244,6 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   gather(0, 0);
 
   // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q; then k . q; append k, alpha ----
-  bf16x8_t sf[kKS][2];
   {
     const int g = tid >> 4, j = tid & 15;
     const int ngroups = nthreads >> 4;
@@ -255,20 +284,6 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
         al_wr[own] = beamAl[bb];
       }
     }
-    // this wave's 16 rows of S_ctx, bf16 high and low halves, resident for the rest of the tile;
-    // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16, and
-    // wave x takes the block w = x / 2, mi = x % 2
-    {
-      const int W = d_v / 32;
-      const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
-      const u32x4_t* __restrict__ fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
-          sf[ks][hl] = __builtin_bit_cast(
-              bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
-    }
   }
   __syncthreads();
 
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
       p[e] = A * pk[e];
       sq[e] = A * pq[e];
     }
-    const f32x2_t vv = V[mt];
+    const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bc * lay.vrow + dv0 * 2);
     for (int m0 = 0; m0 < nch; m0 += kChunk) {
       if (m0 > 0) gather(mt, m0);
 #pragma unroll
@@ -339,8 +354,7 @@ bool fused_supported(int d_k, int d_v, int L_max) {
 }
 
 size_t fused_lds_bytes(int tile, int L_max, int d_v) {
-  (void)d_v;
-  return (size_t)fused_layout(tile, L_max).total;
+  return (size_t)fused_layout(tile, L_max, d_v).total;
 }
 
 int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
@@ -349,7 +363,7 @@ int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
   const int cands[3] = {64, 32, 16};
   for (int c : cands) {
     const long wgs = G * ((n + c - 1) / c);
-    if (wgs >= 1024 && fused_lds_bytes(c, L_max, d_v) <= 64 * 1024) return c;
+    if (wgs >= 1024 && fused_lds_bytes(c, L_max, d_v) <= lds_budget(d_v)) return c;
   }
   return 16;
 }
