@@ -12,6 +12,8 @@ Prints one JSON line.  Extra objects:
   cpu_baseline  the float64 CPU oracle (record-replay form) timed on whole requests of the same workload
   fullstate     the controlled FullState path (dense per-beam state) on the same inputs
   hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
+  beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
+                request), timed on its own with HIP events; not part of the decode step above
 """
 
 from __future__ import annotations
@@ -99,6 +101,37 @@ def hbm_probe(torch, dev, gib: float = 2.0):
     return res
 
 
+def select_bench(torch, dev, cfg, n_cand: int = 256, reps: int = 20, with_cpu: bool = True):
+    """Beam selection at the workload's shape: R requests, B current beams x n_cand candidates -> B survivors."""
+    from linear_attention_beam_amd import inputs, onela
+    R, n_prev, n_beams = cfg.R, cfg.B, cfg.B
+    si = inputs.select_inputs(R, n_prev, n_cand, seed=0)
+    bs = torch.from_numpy(si.beam_scores).to(dev)
+    lp = torch.from_numpy(si.logp).to(dev)
+    need = onela.onela_beam_select_scratch(R, n_prev, n_cand, n_beams)
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        onela.beam_select(bs, lp, n_beams, scratch=scratch)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        onela.beam_select(bs, lp, n_beams, scratch=scratch)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = R * n_prev * n_cand * 4 + R * n_prev * 4 + R * n_beams * 12
+    out = {"shape": f"R={R} n_prev={n_prev} n_cand={n_cand} -> n_beams={n_beams}", "us_per_call": us,
+           "candidates_per_s": R * n_prev * n_cand / (us * 1e-6), "algorithmic_bytes": nbytes,
+           "achieved_GBs": nbytes / (us * 1e-6) / 1e9}
+    if with_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.beam_select(si.beam_scores, si.logp, n_beams)
+        out["cpu_oracle_ms"] = (time.perf_counter() - t0) * 1e3
+    return out
+
+
 def cpu_baseline(cfg, steps, budget_s: float):
     """Time the CPU oracle's record-replay decode on whole requests (every head, beam and step)."""
     import oracle
@@ -146,6 +179,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU-baseline work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullstate", action="store_true")
+    ap.add_argument("--no-select", action="store_true", help="skip the beam-selection measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the benchmark, run a 1 GiB float32 elementwise copy three times (reads 1 GiB, writes "
                          "1 GiB) so hardware counters of a known-size transfer sit in the same profile")
@@ -277,6 +311,9 @@ def main():
         "context_ms": context_ms,
     }
     line["hbm_probe"] = hbm_probe(torch, dev)
+    if not args.no_select:
+        line["beam_select"] = select_bench(torch, dev, cfg, with_cpu=not args.no_cpu_baseline)
+        log(f"[bench] beam selection {line['beam_select']['shape']}: {line['beam_select']['us_per_call']:.1f} us/call")
     sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
     del view
     ctx.close()

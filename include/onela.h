@@ -155,6 +155,30 @@ onela_status onela_get_status(onela_handle h, void* stream);
 /* Fill *view with the current decode state (host-side only; no synchronisation). */
 onela_status onela_get_view(onela_handle h, onela_view* view);
 
+/* ---- Beam selection (stateless; no handle) ----------------------------------------------------------
+ * The step that produces the next decode step's parents: beams are pruned, reordered and fanned out, each
+ * survivor naming its parent ("Scientific Impact Assessment: OneLA", §1 Core Contribution).  The pages do
+ * not state the rule; this is the plain beam-search step.  For each request r, every current beam b (of
+ * n_prev) proposes every candidate token c (of n_cand) with the float32 score
+ *     s = d_beam_scores[r][b] + d_logp[r][b][c]      (one addition, round to nearest even);
+ * the n_beams candidates with the highest scores survive, best first, equal scores ordered by the smaller
+ * flat index b * n_cand + c (-0 and +0 are equal).  Survivor i of request r is written as
+ *     d_parent_idx[r][i] = b,  d_token[r][i] = c,  d_scores[r][i] = s,
+ * so d_parent_idx can be passed straight to onela_step and d_scores become the next beam scores.
+ *   d_beam_scores [R][n_prev] float32, d_logp [R][n_prev][n_cand] float32 (finite or -inf; NaN has no
+ *   rank and gives unspecified survivors), outputs [R][n_beams].
+ * d_scratch: device memory of at least onela_beam_select_scratch(...) bytes (may be NULL when that is 0),
+ * owned by the caller; the call allocates nothing.  All device pointers must stay valid until the stream
+ * reaches the work.  Errors (host-side, nothing enqueued): ONELA_ERR_INVALID_ARG for sizes < 1, n_beams >
+ * n_prev * n_cand, n_prev * n_cand >= 2^31, a NULL buffer or a scratch smaller than required;
+ * ONELA_ERR_UNSUPPORTED for n_beams > 2048; ONELA_ERR_DEVICE for a failed launch. */
+onela_status onela_beam_select_scratch(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                                       size_t* bytes);
+onela_status onela_beam_select(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                               const float* d_beam_scores, const float* d_logp, int32_t* d_parent_idx,
+                               int32_t* d_token, float* d_scores, void* d_scratch, size_t scratch_bytes,
+                               void* stream);
+
 /* Static text for a status code; message of this thread's last failing call ("" if none). */
 const char* onela_status_string(onela_status s);
 const char* onela_last_error(void);

@@ -50,6 +50,13 @@ int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested);
 size_t fused_lds_bytes(int tile, int L_max, int d_v);
 hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s);
 
+// Beam selection: top n_beams of beam_score + logp per request, best first (beam_select.hip).
+int beam_select_max_beams();
+size_t beam_select_scratch_bytes(int R, long n, int n_beams);
+hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R, int n_prev, int n_cand,
+                              int n_beams, int32_t* parent, int32_t* token, float* score, void* scratch,
+                              hipStream_t s);
+
 hipError_t launch_fullstate(const StepArgs& a, bool bf16, const int32_t* parent, int b_prev, const float* fs_prev,
                             float* fs_next, hipStream_t s);
 

@@ -349,6 +349,46 @@ onela_status onela_get_view(onela_handle h, onela_view* view) {
   return ok();
 }
 
+static onela_status select_args(int32_t R, int32_t n_prev, int32_t n_cand, int32_t n_beams) {
+  if (R < 1 || n_prev < 1 || n_cand < 1 || n_beams < 1)
+    return fail(ONELA_ERR_INVALID_ARG, "num_requests (%d), n_prev (%d), n_cand (%d) and n_beams (%d) must be >= 1",
+                R, n_prev, n_cand, n_beams);
+  const long n = (long)n_prev * n_cand;
+  if (n >= 2147483648L) return fail(ONELA_ERR_INVALID_ARG, "n_prev * n_cand (%ld) must be below 2^31", n);
+  if (n_beams > n) return fail(ONELA_ERR_INVALID_ARG, "n_beams (%d) exceeds the %ld candidates", n_beams, n);
+  if (n_beams > beam_select_max_beams())
+    return fail(ONELA_ERR_UNSUPPORTED, "n_beams (%d) above %d", n_beams, beam_select_max_beams());
+  if ((double)R * n >= 9.0e15) return fail(ONELA_ERR_INVALID_ARG, "selection too large");
+  return ONELA_OK;
+}
+
+onela_status onela_beam_select_scratch(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                                       size_t* bytes) {
+  if (!bytes) return fail(ONELA_ERR_INVALID_ARG, "bytes is NULL");
+  const onela_status st = select_args(num_requests, n_prev, n_cand, n_beams);
+  if (st != ONELA_OK) return st;
+  *bytes = beam_select_scratch_bytes(num_requests, (long)n_prev * n_cand, n_beams);
+  return ok();
+}
+
+onela_status onela_beam_select(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                               const float* d_beam_scores, const float* d_logp, int32_t* d_parent_idx,
+                               int32_t* d_token, float* d_scores, void* d_scratch, size_t scratch_bytes,
+                               void* stream) {
+  onela_status st = select_args(num_requests, n_prev, n_cand, n_beams);
+  if (st != ONELA_OK) return st;
+  if (!d_beam_scores || !d_logp || !d_parent_idx || !d_token || !d_scores)
+    return fail(ONELA_ERR_INVALID_ARG, "a beam-selection buffer is NULL");
+  const size_t need = beam_select_scratch_bytes(num_requests, (long)n_prev * n_cand, n_beams);
+  if (need > 0 && (!d_scratch || scratch_bytes < need))
+    return fail(ONELA_ERR_INVALID_ARG, "scratch of %zu bytes is smaller than the %zu required", scratch_bytes, need);
+  st = launched(launch_beam_select(d_beam_scores, d_logp, num_requests, n_prev, n_cand, n_beams, d_parent_idx,
+                                   d_token, d_scores, need > 0 ? d_scratch : nullptr,
+                                   static_cast<hipStream_t>(stream)),
+                "beam selection");
+  return st != ONELA_OK ? st : ok();
+}
+
 const char* onela_status_string(onela_status s) {
   switch (s) {
     case ONELA_OK: return "ONELA_OK";

@@ -23,8 +23,9 @@ Recipe (every configuration):
   * Streams: numpy PCG64 generators seeded by SeedSequence([0x0E1A, config index, stream, seed, ...]):
     stream 0 draws S_ctx (one generator) or the prefill inputs (one generator per request, drawing
     k, v, alpha, beta in that order); stream 1 the decode inputs (one generator per step and request,
-    drawing q, k, v, alpha, beta); stream 2 the parents (one generator per step).  Chunks are drawn in
-    parallel threads; the values do not depend on the thread count.
+    drawing q, k, v, alpha, beta); stream 2 the parents (one generator per step); stream 3 the
+    candidate scores of the beam selection (``select_inputs``).  Chunks are drawn in parallel threads;
+    the values do not depend on the thread count.
 """
 
 from __future__ import annotations
@@ -39,7 +40,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "config", "StepInputs", "PrefillInputs",
     "decode_inputs", "prefill_inputs", "direct_sctx", "parents_for_step",
-    "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "SelectInputs", "select_inputs",
 ]
 
 _SEED_TAG = 0x0E1A
@@ -234,3 +235,31 @@ def prefill_inputs(cfg: Config, seed: int = 0, steps: Optional[int] = None, requ
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(len(reqs))))
     return PrefillInputs(k, v, alpha, beta)
+
+
+@dataclasses.dataclass
+class SelectInputs:
+    """Inputs of one beam-selection step: beam_scores [R, n_prev] and logp [R, n_prev, n_cand], float32."""
+
+    beam_scores: np.ndarray
+    logp: np.ndarray
+
+
+def select_inputs(R: int, n_prev: int, n_cand: int, seed: int = 0, tag: int = 0, ties: bool = False) -> SelectInputs:
+    """Synthetic candidate scores for the beam selection that precedes a decode step.
+
+    Stream 3 of the seed sequence.  Per request: beam scores are minus the running sums of Exp(1) draws
+    (best beam first, as the score-rank order of the parents); candidate log-probabilities are a
+    log-softmax, in float64, of N(0, 2^2) logits, rounded once to float32.  With ``ties`` the logits are
+    drawn from 8 integer levels and the beam scores from 4, so many candidate scores are exactly equal.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([_SEED_TAG, 3, tag, seed, R, n_prev, n_cand])))
+    if ties:
+        bs = -rng.integers(0, 4, size=(R, n_prev)).astype(np.float64)
+        logits = rng.integers(0, 8, size=(R, n_prev, n_cand)).astype(np.float64)
+    else:
+        bs = -np.cumsum(rng.exponential(1.0, size=(R, n_prev)), axis=1)
+        logits = 2.0 * rng.standard_normal((R, n_prev, n_cand))
+    m = logits.max(axis=2, keepdims=True)
+    lse = m + np.log(np.exp(logits - m).sum(axis=2, keepdims=True))
+    return SelectInputs(bs.astype(np.float32), (logits - lse).astype(np.float32))

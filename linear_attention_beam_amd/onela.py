@@ -61,6 +61,10 @@ _SIGNATURES = {
     "onela_reset": [_P, _P],
     "onela_get_status": [_P, _P],
     "onela_get_view": [_P, ctypes.POINTER(onela_view)],
+    "onela_beam_select_scratch": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.POINTER(ctypes.c_size_t)],
+    "onela_beam_select": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                          ctypes.c_size_t, _P],
     "onela_status_string": [ctypes.c_int],
     "onela_last_error": [],
 }
@@ -144,9 +148,49 @@ def onela_get_view(h: int) -> onela_view:
     return v
 
 
+def onela_beam_select_scratch(R: int, n_prev: int, n_cand: int, n_beams: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().onela_beam_select_scratch(R, n_prev, n_cand, n_beams, ctypes.byref(n)), "onela_beam_select_scratch")
+    return n.value
+
+
+def onela_beam_select(R: int, n_prev: int, n_cand: int, n_beams: int, beam_scores_ptr: int, logp_ptr: int,
+                      parent_ptr: int, token_ptr: int, scores_ptr: int, scratch_ptr: Optional[int], scratch_bytes: int,
+                      stream: int) -> None:
+    _check(lib().onela_beam_select(R, n_prev, n_cand, n_beams, beam_scores_ptr, logp_ptr, parent_ptr, token_ptr,
+                                   scores_ptr, scratch_ptr, scratch_bytes, stream), "onela_beam_select")
+
+
 # ---------------------------------------------------------------------------------------------------
-# PyTorch convenience wrapper
+# PyTorch convenience wrappers
 # ---------------------------------------------------------------------------------------------------
+
+def beam_select(beam_scores, logp, n_beams: int, scratch=None):
+    """Top n_beams of beam_scores[r, b] + logp[r, b, c] per request, best first (see onela_beam_select).
+
+    beam_scores: [R, n_prev] float32, logp: [R, n_prev, n_cand] float32, both contiguous on one GPU.
+    Returns (parent int32 [R, n_beams], token int32 [R, n_beams], scores float32 [R, n_beams]).  ``scratch``
+    (a uint8 device tensor of at least onela_beam_select_scratch bytes) is allocated here when not given.
+    """
+    import torch
+    R, n_prev, n_cand = (int(x) for x in logp.shape)
+    dev = logp.device
+    for name, x, shape in (("beam_scores", beam_scores, (R, n_prev)), ("logp", logp, (R, n_prev, n_cand))):
+        if x.device != dev or x.dtype != torch.float32 or tuple(x.shape) != shape or not x.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous float32 {shape} on {dev}, got {x.dtype} "
+                             f"{tuple(x.shape)} on {x.device}")
+    need = onela_beam_select_scratch(R, n_prev, n_cand, n_beams)
+    if scratch is None and need:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    parent = torch.empty((R, n_beams), dtype=torch.int32, device=dev)
+    token = torch.empty((R, n_beams), dtype=torch.int32, device=dev)
+    scores = torch.empty((R, n_beams), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        onela_beam_select(R, n_prev, n_cand, n_beams, beam_scores.data_ptr(), logp.data_ptr(), parent.data_ptr(),
+                          token.data_ptr(), scores.data_ptr(), scratch.data_ptr() if need else None,
+                          scratch.numel() if need else 0, torch.cuda.current_stream(dev).cuda_stream)
+    return parent, token, scores
+
 
 class OneLA:
     """A decode context on one GPU: R requests x H heads, up to max_beams beams and max_steps steps.

@@ -77,3 +77,24 @@ def test_status_strings():
     for code in range(7):
         assert onela.status_name(code).startswith("ONELA_")
     assert onela.status_name(99) == "unknown onela_status"
+
+
+@pytest.mark.parametrize("R,n_prev,n_cand,n_beams", [(32, 512, 256, 512), (1, 1, 5, 3), (2, 64, 64, 2048),
+                                                     (3, 100, 300, 700), (1, 128, 128, 100)])
+def test_beam_select_scratch(R, n_prev, n_cand, n_beams):
+    """Two buffers of the keys that survive the first reduce pass over 8192-key chunks; none when a request has
+    at most 8192 candidates (one workgroup selects them directly)."""
+    n = n_prev * n_cand
+    expect = 0 if n <= 8192 else 2 * R * ((n + 8191) // 8192) * n_beams * 8
+    assert onela.onela_beam_select_scratch(R, n_prev, n_cand, n_beams) == expect
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 8, 1), onela.ONELA_ERR_INVALID_ARG), ((1, 4, 8, 33), onela.ONELA_ERR_INVALID_ARG),
+    ((1, 4, 8, 0), onela.ONELA_ERR_INVALID_ARG), ((1, 65536, 65536, 8), onela.ONELA_ERR_INVALID_ARG),
+    ((1, 64, 64, 2049), onela.ONELA_ERR_UNSUPPORTED),
+])
+def test_beam_select_bad_args(args, status):
+    with pytest.raises(onela.OnelaError) as e:
+        onela.onela_beam_select_scratch(*args)
+    assert e.value.status == status
