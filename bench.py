@@ -11,6 +11,8 @@ Prints one JSON line.  Extra objects:
                 the run's own chain tables) / its average launch time from HIP events in the timed region
   cpu_baseline  the float64 CPU oracle (record-replay form) timed on whole requests of the same workload
   fullstate     the controlled FullState path (dense per-beam state) on the same inputs
+  materialize   the materializing-replay path (each beam's dense parent state rebuilt every step) on the same
+                inputs
   hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
@@ -180,6 +182,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullstate", action="store_true")
     ap.add_argument("--no-select", action="store_true", help="skip the beam-selection measurement")
+    ap.add_argument("--no-materialize", action="store_true", help="skip the materializing-replay comparison")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the benchmark, run a 1 GiB float32 elementwise copy three times (reads 1 GiB, writes "
                          "1 GiB) so hardware counters of a known-size transfer sit in the same profile")
@@ -347,6 +350,35 @@ def main():
         log(f"[bench] FullState: {fs_ms:.3f} ms/decode; replay is {fs_ms / ms_per_step:.1f}x faster")
         fs.close()
         del fs
+
+    if not args.no_materialize:
+        mz = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, materialize=True,
+                         device=dev)
+        mz.set_context(torch.from_numpy(sctx_host).to(dev))
+
+        def mz_decode():
+            mz.reset()
+            for t in range(cfg.L):
+                mz.step(**dsteps[t], out=outs[t])
+
+        mz_decode()
+        torch.cuda.synchronize()
+        reps = 3
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            mz_decode()
+        b.record(stream)
+        torch.cuda.synchronize()
+        mz_ms = a.elapsed_time(b) / reps
+        flops = sum(2.0 * cfg.R * cfg.B * cfg.H * cfg.d_k * cfg.d_v * (t + 2) for t in range(cfg.L))
+        line["materialize"] = {"ms_per_step": mz_ms, "beam_tokens_per_s": cfg.beam_tokens / (mz_ms * 1e-3),
+                               "fp32_flops_per_decode": flops, "achieved_TFLOPs": flops / (mz_ms * 1e-3) / 1e12,
+                               "replay_speedup": mz_ms / ms_per_step}
+        log(f"[bench] materializing replay: {mz_ms:.3f} ms/decode; projection replay is {mz_ms / ms_per_step:.1f}x "
+            "faster")
+        mz.close()
+        del mz
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, steps, args.cpu_budget)

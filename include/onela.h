@@ -75,8 +75,13 @@ typedef enum {
 
 /* onela_config.flags */
 enum {
-  ONELA_FLAG_FORCE_GENERIC = 1 /* replay mode: run the plain fp32-FMA kernel even where the fused
-                                  bf16-MFMA kernel applies (for A/B checks) */
+  ONELA_FLAG_FORCE_GENERIC = 1, /* replay mode: run the plain fp32-FMA kernel even where the fused
+                                   bf16-MFMA kernel applies (for A/B checks) */
+  ONELA_FLAG_MATERIALIZE = 2    /* replay mode: comparison path that rebuilds every beam's dense parent
+                                   state from S_ctx and its chain each step, then projects it
+                                   ("Scientific Impact Assessment: OneLA", §1 and "Additional
+                                   Observations": the replay of shared history that the method avoids).
+                                   Same records, index and outputs as the projection replay. */
 };
 
 typedef struct {

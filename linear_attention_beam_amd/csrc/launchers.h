@@ -43,6 +43,8 @@ hipError_t launch_prefill(const float* k, const float* v, const float* alpha, co
 bool prefill_supported(int d_k, int d_v);
 
 hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
+// Materializing replay (comparison path): dense parent state rebuilt per pair and step.
+hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t s);
 
 // Fused bf16-MFMA step (d_k == 128, d_v % 32 == 0, d_v <= 256).  tile_beams 0 = automatic.
 bool fused_supported(int d_k, int d_v, int L_max);

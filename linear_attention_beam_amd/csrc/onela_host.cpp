@@ -19,6 +19,7 @@ struct onela_ctx {
   size_t ws_bytes;
   int device;
   bool fused;
+  bool materialize;
   int* flag;
   float* sctx_t;
   uint16_t* sctx_frag;
@@ -76,7 +77,8 @@ onela_status check_config(const onela_config* c) {
     return fail(ONELA_ERR_INVALID_ARG, "qkv_dtype %d is not ONELA_F32 or ONELA_BF16", c->qkv_dtype);
   if (c->mode != ONELA_MODE_REPLAY && c->mode != ONELA_MODE_FULLSTATE)
     return fail(ONELA_ERR_INVALID_ARG, "mode %d is not REPLAY or FULLSTATE", c->mode);
-  if (c->flags & ~ONELA_FLAG_FORCE_GENERIC) return fail(ONELA_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+  if (c->flags & ~(ONELA_FLAG_FORCE_GENERIC | ONELA_FLAG_MATERIALIZE))
+    return fail(ONELA_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
   if (c->tile_beams != 0 && c->tile_beams != 16 && c->tile_beams != 32 && c->tile_beams != 64 &&
       c->tile_beams != 128)
     return fail(ONELA_ERR_INVALID_ARG, "tile_beams %d is not 0, 16, 32, 64 or 128", c->tile_beams);
@@ -97,7 +99,7 @@ Layout make_layout(const onela_config* c) {
   const size_t R = c->num_requests, H = c->num_heads, dk = c->d_k, dv = c->d_v;
   const size_t B = c->max_beams, L = c->max_steps, slots = B * L;
   const size_t in_bytes = c->qkv_dtype == ONELA_BF16 ? 2 : 4;
-  l.fused = c->mode == ONELA_MODE_REPLAY && c->qkv_dtype == ONELA_BF16 && !(c->flags & ONELA_FLAG_FORCE_GENERIC) &&
+  l.fused = c->mode == ONELA_MODE_REPLAY && c->qkv_dtype == ONELA_BF16 && !(c->flags & (ONELA_FLAG_FORCE_GENERIC | ONELA_FLAG_MATERIALIZE)) &&
             fused_supported(c->d_k, c->d_v, c->max_steps);
   size_t off = 0;
   l.flag = off;       off += 256;
@@ -185,6 +187,7 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
   h->ws_bytes = workspace_bytes;
   h->device = dev;
   h->fused = l.fused;
+  h->materialize = cfg->mode == ONELA_MODE_REPLAY && (cfg->flags & ONELA_FLAG_MATERIALIZE);
   h->flag = reinterpret_cast<int*>(ws + l.flag);
   h->sctx_t = reinterpret_cast<float*>(ws + l.sctx_t);
   h->sctx_frag = l.fused ? reinterpret_cast<uint16_t*>(ws + l.sctx_frag) : nullptr;
@@ -303,7 +306,8 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
   } else if (h->fused) {
     st = launched(launch_step_fused(a, tile, s), "fused step");
   } else {
-    st = launched(launch_step_generic(a, bf16, s), "step");
+    st = h->materialize ? launched(launch_step_materialize(a, bf16, s), "materializing step")
+                        : launched(launch_step_generic(a, bf16, s), "step");
   }
   if (st != ONELA_OK) return st;
   h->t = t;

@@ -28,6 +28,7 @@ ONELA_BF16 = 1
 ONELA_MODE_REPLAY = 0
 ONELA_MODE_FULLSTATE = 1
 ONELA_FLAG_FORCE_GENERIC = 1
+ONELA_FLAG_MATERIALIZE = 2
 
 
 class onela_config(ctypes.Structure):
@@ -196,18 +197,20 @@ class OneLA:
     """A decode context on one GPU: R requests x H heads, up to max_beams beams and max_steps steps.
 
     qkv_dtype: "bf16" or "f32"; mode: "replay" (shared state + records) or "fullstate" (comparison).
+    materialize: in replay mode, rebuild every beam's dense parent state each step (comparison path).
     """
 
     def __init__(self, R: int, H: int, d_k: int, d_v: int, max_beams: int, max_steps: int,
                  qkv_dtype: str = "bf16", mode: str = "replay", force_generic: bool = False,
-                 tile_beams: int = 0, device=None):
+                 tile_beams: int = 0, device=None, materialize: bool = False):
         import torch
         self._torch = torch
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.cfg = onela_config(R, H, d_k, d_v, max_beams, max_steps,
                                 ONELA_BF16 if qkv_dtype == "bf16" else ONELA_F32,
                                 ONELA_MODE_FULLSTATE if mode == "fullstate" else ONELA_MODE_REPLAY,
-                                ONELA_FLAG_FORCE_GENERIC if force_generic else 0, tile_beams)
+                                (ONELA_FLAG_FORCE_GENERIC if force_generic else 0)
+                                | (ONELA_FLAG_MATERIALIZE if materialize else 0), tile_beams)
         if qkv_dtype not in ("bf16", "f32") or mode not in ("replay", "fullstate"):
             raise ValueError(f"qkv_dtype {qkv_dtype!r} / mode {mode!r}")
         self.qkv_torch_dtype = torch.bfloat16 if qkv_dtype == "bf16" else torch.float32

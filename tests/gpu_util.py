@@ -72,14 +72,14 @@ class GpuRun:
     """One decode through libonela.  ``outs[t]`` stays on the device."""
 
     def __init__(self, cfg: inputs.Config, steps, sctx=None, prefill=None, mode="replay", force_generic=False,
-                 tile_beams=0, max_beams=None, max_steps=None, sctx_out=False):
+                 tile_beams=0, max_beams=None, max_steps=None, sctx_out=False, materialize=False):
         dev = device()
         self.cfg = cfg
         self.max_beams = cfg.B if max_beams is None else max_beams
         self.max_steps = len(steps) if max_steps is None else max_steps
         self.ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, self.max_beams, self.max_steps,
                                qkv_dtype=cfg.qkv_dtype, mode=mode, force_generic=force_generic,
-                               tile_beams=tile_beams, device=dev)
+                               tile_beams=tile_beams, device=dev, materialize=materialize)
         self.sctx_gpu = None
         if sctx is not None:
             self.ctx.set_context(torch.from_numpy(np.asarray(sctx, np.float32)).to(dev))

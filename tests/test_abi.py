@@ -56,7 +56,8 @@ def expected_bytes(c):
 
 @pytest.mark.parametrize("kw", [
     {}, dict(d_v=256), dict(qkv_dtype=onela.ONELA_F32, d_k=16, d_v=16), dict(mode=onela.ONELA_MODE_FULLSTATE),
-    dict(flags=onela.ONELA_FLAG_FORCE_GENERIC), dict(d_k=64, d_v=100), dict(max_steps=64, max_beams=1),
+    dict(flags=onela.ONELA_FLAG_FORCE_GENERIC), dict(flags=onela.ONELA_FLAG_MATERIALIZE), dict(d_k=64, d_v=100),
+    dict(max_steps=64, max_beams=1),
 ])
 def test_workspace_size(kw):
     c = cfg(**kw)

@@ -183,3 +183,18 @@ def test_context_transpose_is_exact():
     ctx.set_context(torch.from_numpy(sctx).to(dev))
     torch.cuda.synchronize()
     assert np.array_equal(ctx.view()["sctx_t"].cpu().numpy(), np.swapaxes(sctx, -1, -2))
+
+
+@pytest.mark.parametrize("d_k,d_v,dtype", [(130, 72, "f32"), (64, 256, "bf16"), (256, 256, "bf16"), (16, 16, "f32"),
+                                            (128, 128, "bf16")])
+def test_materializing_replay(d_k, d_v, dtype):
+    """The comparison path that rebuilds each beam's dense parent state: every head against the oracle, including
+    uneven column groups (d_k = 130 splits 44/43/43) and the 1024-thread case (d_k = d_v = 256)."""
+    cfg = inputs.config(2, R=2, H=2, d_k=d_k, d_v=d_v, B=40, L=4, qkv_dtype=dtype)
+    gu.log(f"materializing replay d_k={d_k} d_v={d_v} {dtype}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, materialize=True)
+    assert not run.view["fused"]
+    assert run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")

@@ -56,12 +56,12 @@ def c1():
     return cfg, pf, sctx, steps, refs, chains
 
 
-@pytest.mark.parametrize("variant", ["fused", "generic", "fullstate"])
+@pytest.mark.parametrize("variant", ["fused", "generic", "fullstate", "materialize"])
 def test_c1_every_head(c1, variant):
     cfg, pf, sctx, steps, refs, chains = c1
     gu.log(f"R=1 H=16 B=128 L=4, variant={variant}")
     run = gu.GpuRun(cfg, steps, sctx=sctx, mode="fullstate" if variant == "fullstate" else "replay",
-                    force_generic=variant == "generic")
+                    force_generic=variant == "generic", materialize=variant == "materialize")
     assert run.view["fused"] == (variant == "fused")
     assert run.status == onela.ONELA_OK
     worst = (0.0, 0.0)
