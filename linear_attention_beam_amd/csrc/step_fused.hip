@@ -4,8 +4,9 @@
 //
 // Workgroup = (request, head, tile of NB beams); d_v / 16 waves of 64 lanes (d_k = 128 fixed).
 //   Phase 0  everything that needs nothing from the ancestry goes out in the first round trip: parents,
-//            alpha and beta; k, q and v rows of the tile, staged in LDS with 16-byte loads; this wave's
-//            S_ctx rows.  Wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay
+//            alpha and beta; k, q and v rows of the tile (16-byte loads, held in registers and written to
+//            LDS only after the chain rows are requested, so that the two round trips overlap); this
+//            wave's S_ctx rows.  Wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay
 //            in registers for the whole tile (each S_ctx element is read once per tile and reused by all
 //            NB beams).  Then the ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each
 //            beam's chain is its parent's chain from the previous table plus its own slot; the head-0
@@ -35,6 +36,8 @@ constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
 constexpr int kItems = 4;            // chain keys in flight per 16-lane group (phase 1)
 constexpr int kChunk = 4;            // chain records in flight per beam (phase 2)
+constexpr int kPX = 4;               // 16-byte pieces of the k and q rows per thread held in registers
+constexpr int kPV = 2;               // 16-byte pieces of the v rows per thread held in registers
 
 struct FusedLds {
   int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, vs, vrow, total;
@@ -135,22 +138,50 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
     beamAl[bb] = live ? a.alpha[in_row(bb)] : 0.f;
     beamBe[bb] = live ? a.beta[in_row(bb)] : 0.f;
   }
-  for (int idx = tid; idx < NB * 32; idx += nthreads) {
-    const int row = idx >> 4, c = idx & 15;  // row < NB: key rows, row >= NB: query rows
+  // k, q and v of the tile go to registers now and to LDS only after the chain rows are requested, so
+  // the chain round trip overlaps this one
+  const int vc = d_v >> 3;  // 16-byte pieces per v row
+  auto x_piece = [&](int idx) -> u32x4_t {  // idx < NB * 32; rows < NB are keys, the others queries
+    const int row = idx >> 4, c = idx & 15;
     const int bb = row < NB ? row : row - NB;
     u32x4_t val = {0u, 0u, 0u, 0u};
     if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)bb * hk + c * 8);
-    *reinterpret_cast<u32x4_t*>(xs + row * kXRow + c * 16) = val;
-  }
-  {
-    const int vc = d_v >> 3;  // 16-byte pieces per v row
-    for (int idx = tid; idx < NB * vc; idx += nthreads) {
-      const int bb = idx / vc, c = idx - bb * vc;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (bb < nb) val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)bb * hv + c * 8);
-      *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + c * 16) = val;
+    return val;
+  };
+  auto v_piece = [&](int idx) -> u32x4_t {  // idx < NB * vc
+    const int bb = idx / vc, c = idx - bb * vc;
+    u32x4_t val = {0u, 0u, 0u, 0u};
+    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)bb * hv + c * 8);
+    return val;
+  };
+  u32x4_t XR[kPX], VR[kPV];
+#pragma unroll
+  for (int u = 0; u < kPX; ++u)
+    if (tid + u * nthreads < NB * 32) XR[u] = x_piece(tid + u * nthreads);
+#pragma unroll
+  for (int u = 0; u < kPV; ++u)
+    if (tid + u * nthreads < NB * vc) VR[u] = v_piece(tid + u * nthreads);
+  auto store_x = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPX; ++u) {
+      const int idx = tid + u * nthreads;
+      if (idx < NB * 32) *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = XR[u];
     }
-  }
+    for (int idx = tid + kPX * nthreads; idx < NB * 32; idx += nthreads)
+      *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = x_piece(idx);
+#pragma unroll
+    for (int u = 0; u < kPV; ++u) {
+      const int idx = tid + u * nthreads;
+      if (idx < NB * vc) {
+        const int bb = idx / vc;
+        *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = VR[u];
+      }
+    }
+    for (int idx = tid + kPV * nthreads; idx < NB * vc; idx += nthreads) {
+      const int bb = idx / vc;
+      *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = v_piece(idx);
+    }
+  };
   const int gq = lane >> 4, col = lane & 15;
   const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
   constexpr int kTiles = NB / 16;
@@ -173,9 +204,9 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   // ---- phase 0 (cont.): the parents' chain rows and decay rows in one round trip; this step's rows ----
   const int drow = L + 1;    // decay row: c_0 .. c_{L-1}, then A
   const int nper = nch + 1;  // per beam: nch chain entries, then the parent's total decay A
-  for (int base = 0; base < nb * nper; base += 4 * nthreads) {
-    int raw[4];
-    float dec[4];
+  int raw[4];
+  float dec[4];
+  auto chain_load = [&](int base) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + u * nthreads + tid;
@@ -191,6 +222,11 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
         }
       }
     }
+  };
+  chain_load(0);
+  store_x();
+  for (int base = 0; base < nb * nper; base += 4 * nthreads) {
+    if (base > 0) chain_load(base);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + u * nthreads + tid;
