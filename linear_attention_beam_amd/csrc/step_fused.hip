@@ -123,44 +123,37 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   float* __restrict__ al_wr = a.rec_alpha + arena;
   auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
 
-  // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers ----
-  for (int bb = tid; bb < NB; bb += nthreads) {
-    const bool live = bb < nb;
-    int p = 0;
-    if (live) {
-      p = a.parent[(size_t)r * n + b0 + bb];
-      if (p < 0 || p >= a.b_prev) {  // sticky flag; decode as a child of beam 0 so accesses stay in bounds
-        *a.flag = a.epoch;
-        p = 0;
-      }
-    }
-    beamPar[bb] = p;
-    beamAl[bb] = live ? a.alpha[in_row(bb)] : 0.f;
-    beamBe[bb] = live ? a.beta[in_row(bb)] : 0.f;
-  }
+  // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers.  Every load
+  // goes out before the first value is used: thread tid < NB keeps beam tid's parent, alpha and beta in
+  // registers until the k, q, v and S_ctx requests have been issued (nthreads = 4 d_v >= NB). ----
+  // loads are issued unconditionally (clamped indices, values dropped afterwards) so that the compiler can
+  // count them exactly and later waits do not cover loads issued after the one they need
+  const int tb = min(tid, nb - 1);
+  int pP = a.parent[(size_t)r * n + b0 + tb];
+  float pAl = a.alpha[in_row(tb)];
+  float pBe = a.beta[in_row(tb)];
+  __builtin_amdgcn_sched_barrier(0);  // keep these first in issue order
   // k, q and v of the tile go to registers now and to LDS only after the chain rows are requested, so
   // the chain round trip overlaps this one
   const int vc = d_v >> 3;  // 16-byte pieces per v row
   auto x_piece = [&](int idx) -> u32x4_t {  // idx < NB * 32; rows < NB are keys, the others queries
     const int row = idx >> 4, c = idx & 15;
     const int bb = row < NB ? row : row - NB;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)bb * hk + c * 8);
+    u32x4_t val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)min(bb, nb - 1) * hk + c * 8);
+    if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
     return val;
   };
   auto v_piece = [&](int idx) -> u32x4_t {  // idx < NB * vc
     const int bb = idx / vc, c = idx - bb * vc;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (bb < nb) val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)bb * hv + c * 8);
+    u32x4_t val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)min(bb, nb - 1) * hv + c * 8);
+    if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
     return val;
   };
   u32x4_t XR[kPX], VR[kPV];
 #pragma unroll
-  for (int u = 0; u < kPX; ++u)
-    if (tid + u * nthreads < NB * 32) XR[u] = x_piece(tid + u * nthreads);
+  for (int u = 0; u < kPX; ++u) XR[u] = x_piece(min(tid + u * nthreads, NB * 32 - 1));
 #pragma unroll
-  for (int u = 0; u < kPV; ++u)
-    if (tid + u * nthreads < NB * vc) VR[u] = v_piece(tid + u * nthreads);
+  for (int u = 0; u < kPV; ++u) VR[u] = v_piece(min(tid + u * nthreads, NB * vc - 1));
   auto store_x = [&]() {
 #pragma unroll
     for (int u = 0; u < kPX; ++u) {
@@ -198,6 +191,21 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
       for (int hl = 0; hl < 2; ++hl)
         sf[ks][hl] = __builtin_bit_cast(
             bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every streaming request is out before the parents are consumed
+  if (tid >= nb) {
+    pP = 0;
+    pAl = 0.f;
+    pBe = 0.f;
+  }
+  if (tid < NB) {
+    if (tid < nb && (pP < 0 || pP >= a.b_prev)) {  // sticky flag; decode as a child of beam 0 so accesses stay in bounds
+      *a.flag = a.epoch;
+      pP = 0;
+    }
+    beamPar[tid] = pP;
+    beamAl[tid] = pAl;
+    beamBe[tid] = pBe;
   }
   __syncthreads();
 
