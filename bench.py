@@ -16,6 +16,9 @@ Prints one JSON line.  Extra objects:
   hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
+  stack         a whole beam-search decode through several GDN layers with random weights (projections as
+                library GEMMs, one decode context per layer, the GPU beam selection between steps) at the
+                workload's R, H, B, L and head sizes; context for the step's share of a model's decode
 """
 
 from __future__ import annotations
@@ -134,6 +137,31 @@ def select_bench(torch, dev, cfg, n_cand: int = 256, reps: int = 20, with_cpu: b
     return out
 
 
+def stack_bench(torch, cfg, layers: int, step_ms: float, reps: int = 3):
+    """Whole beam-search decodes through ``layers`` random-weight GDN layers (hidden size H * d_v, 256
+    candidates), timed end to end with HIP events around the calls on the current stream."""
+    from linear_attention_beam_amd import harness
+    sc = harness.StackConfig(R=cfg.R, B=cfg.B, L=cfg.L, layers=layers, H=cfg.H, d_k=cfg.d_k, d_v=cfg.d_v,
+                             D=cfg.H * cfg.d_v, n_cand=256, prefill_tokens=64, alpha_lo=cfg.alpha_lo)
+    stack = harness.GDNStack(sc)
+    stack.decode()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        stack.decode()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    stack.close()
+    del stack
+    return {"shape": f"layers={layers} D={sc.D} n_cand={sc.n_cand} R={sc.R} H={sc.H} B={sc.B} L={sc.L}",
+            "ms_per_decode": ms, "beam_tokens_per_s": cfg.beam_tokens / (ms * 1e-3),
+            "step_share_est": layers * step_ms / ms,
+            "note": "step_share_est = layers x the decode-step time measured above / this time; the first "
+                    "step decodes min(B, 256) beams, so the share is an upper estimate"}
+
+
 def cpu_baseline(cfg, steps, budget_s: float):
     """Time the CPU oracle's record-replay decode on whole requests (every head, beam and step)."""
     import oracle
@@ -183,6 +211,8 @@ def main():
     ap.add_argument("--no-fullstate", action="store_true")
     ap.add_argument("--no-select", action="store_true", help="skip the beam-selection measurement")
     ap.add_argument("--no-materialize", action="store_true", help="skip the materializing-replay comparison")
+    ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer random-weight decode")
+    ap.add_argument("--stack-layers", type=int, default=4)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the benchmark, run a 1 GiB float32 elementwise copy three times (reads 1 GiB, writes "
                          "1 GiB) so hardware counters of a known-size transfer sit in the same profile")
@@ -379,6 +409,12 @@ def main():
             "faster")
         mz.close()
         del mz
+
+    if not args.no_stack:
+        line["stack"] = stack_bench(torch, cfg, args.stack_layers, ms_per_step)
+        st = line["stack"]
+        log(f"[bench] {args.stack_layers}-layer decode: {st['ms_per_decode']:.3f} ms, "
+            f"{st['beam_tokens_per_s']:.4g} beam-tokens/s; decode steps ~{100 * st['step_share_est']:.0f}%")
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, steps, args.cpu_budget)
