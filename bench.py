@@ -16,6 +16,8 @@ Prints one JSON line.  Extra objects:
   hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
+  prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the fp32
+                vector-ALU peak
   stack         a whole beam-search decode through several GDN layers with random weights (projections as
                 library GEMMs, one decode context per layer, the GPU beam selection between steps) at the
                 workload's R, H, B, L and head sizes; context for the step's share of a model's decode
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector: 256 CUs x 64 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.json")
 FUSED_SRC = os.path.join(ROOT, "linear_attention_beam_amd", "csrc", "step_fused.hip")
 
@@ -134,6 +137,43 @@ def select_bench(torch, dev, cfg, n_cand: int = 256, reps: int = 20, with_cpu: b
         t0 = time.perf_counter()
         oracle.beam_select(si.beam_scores, si.logp, n_beams)
         out["cpu_oracle_ms"] = (time.perf_counter() - t0) * 1e3
+    return out
+
+
+def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool = True):
+    """onela_prefill of the workload's prompt (R x H heads x N tokens, float32 inputs resident in HBM), timed
+    with HIP events on the stream it runs on.  The recurrence is 4 d_k d_v float32 FLOPs per token and head
+    (two FMAs per state element), sequential over tokens: it is bound by the vector ALU, not by HBM."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx.prefill(*ctx_in)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        ctx.prefill(*ctx_in)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    heads, N = cfg.R * cfg.H, cfg.prefill_steps
+    flops = 4.0 * cfg.d_k * cfg.d_v * N * heads
+    nbytes = 4.0 * heads * N * (cfg.d_k + cfg.d_v + 2) + 4.0 * heads * cfg.d_k * cfg.d_v * 3
+    out = {"shape": f"R={cfg.R} H={cfg.H} N={N} d_k={cfg.d_k} d_v={cfg.d_v}", "ms_per_call": ms,
+           "tokens_per_s": cfg.R * N / (ms * 1e-3), "fp32_flops": flops,
+           "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "roofline": {"bound": "alu", "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS},
+           "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+           "note": "call time: the prefill kernel plus the state's transpose and bf16 split"}
+    if with_cpu:
+        import oracle
+        pf_k = ctx_in[0][:1, :, :1].cpu().numpy()
+        pf_v = ctx_in[1][:1, :, :1].cpu().numpy()
+        pf_a = ctx_in[2][:1, :, :1].cpu().numpy()
+        pf_b = ctx_in[3][:1, :, :1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.prefill(pf_k, pf_v, pf_a, pf_b)
+        one = time.perf_counter() - t0
+        out["cpu_oracle_ms_est"] = one * heads * 1e3
+        out["cpu_sample"] = f"one head x {N} tokens in {one * 1e3:.0f} ms, scaled by {heads} heads"
     return out
 
 
@@ -268,9 +308,14 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     context_ms = e0.elapsed_time(e1)
-    del ctx_in
     log(f"[bench] context ready ({'prefill ' + str(cfg.prefill_steps) + ' tokens' if pf else 'set_context'}: "
         f"{context_ms:.2f} ms)")
+    prefill_line = None
+    if pf is not None:
+        prefill_line = prefill_bench(torch, ctx, ctx_in, cfg, stream, with_cpu=not args.no_cpu_baseline)
+        log(f"[bench] prefill: {prefill_line['ms_per_call']:.3f} ms/call, {prefill_line['achieved_TFLOPs']:.1f} "
+            f"TFLOP/s fp32")
+    del ctx_in
 
     def decode(events=None):
         ctx.reset()
@@ -343,6 +388,8 @@ def main():
                      "mfma_frac": mfma_flops / (kernel_ms.sum(axis=1).mean() * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
         "context_ms": context_ms,
     }
+    if prefill_line is not None:
+        line["prefill"] = prefill_line
     line["hbm_probe"] = hbm_probe(torch, dev)
     if not args.no_select:
         line["beam_select"] = select_bench(torch, dev, cfg, with_cpu=not args.no_cpu_baseline)

@@ -132,9 +132,8 @@ onela_status onela_set_context(onela_handle h, const float* d_sctx, void* stream
  * as onela_set_context would ("Scientific Impact Assessment: OneLA", §1: the post-prefill state).
  * d_k: [R][n_tokens][H][d_k], d_v: [R][n_tokens][H][d_v], d_alpha/d_beta: [R][n_tokens][H], all
  * float32.  If d_sctx_out is not NULL the state is also written there as [R][H][d_v][d_k] float32.
- * Needs d_v to divide 256 and d_k / (256 / d_v) to be a power of two no larger than 128 (so d_k * d_v
- * <= 32768): one 256-thread workgroup per (request, head) holds the state in registers.  Other head sizes
- * return ONELA_ERR_UNSUPPORTED; install their context with onela_set_context. */
+ * Any head size the handle accepts (d_k, d_v <= 256); n_tokens = 0 installs the zero state.  The inputs are
+ * read once; the work is 4 d_k d_v float32 FLOPs per token and (request, head). */
 onela_status onela_prefill(onela_handle h, int32_t n_tokens, const float* d_k, const float* d_v,
                            const float* d_alpha, const float* d_beta, float* d_sctx_out, void* stream);
 

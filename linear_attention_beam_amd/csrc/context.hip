@@ -130,104 +130,171 @@ hipError_t launch_split_frag(const float* ST, uint16_t* frag, int RH, int d_v, i
 // GDN prefill from the zero state ("Scientific Impact Assessment: OneLA", §1: the shared post-prefill
 // state), the gated delta rule of Gated DeltaNet (paper index page, "Builds on"):
 //   p = S k,  u = beta (v - alpha p),  S <- alpha S + u k^T.
-// One workgroup of 256 threads per (request, head) keeps S^T in registers: thread (i, part) owns column
-// i of S^T (row i of S) for d_k / NPART consecutive keys, NPART = 256 / d_v.  Token inputs are
-// prefetched one token ahead.
+// Row i of S evolves on its own: it needs v_i and the token's shared k, alpha and beta, nothing from the
+// other rows.  So the recurrence is split over rows, 8 lanes per row: lane j of a row holds the columns of
+// float4 groups j, j + 8, j + 16, ... of d_k (padded with zero columns to a multiple of 32) in registers,
+// and p is summed over the row's 8 lanes with DPP, with no barrier per token.  A workgroup of 1024 threads
+// takes 128 rows of one (request, head).  Tokens come in blocks of kPfT: k, the workgroup's v entries,
+// alpha and beta of a block are staged in LDS (two buffers, one barrier per block), fetched from HBM into
+// registers one block ahead.
+// The decay is carried as a scale, S = g Ŝ with g the running product of alpha: a token then costs one
+// FMA per element for the update, Ŝ += (u / g) k^T.  When g falls below 2^-20 (also when alpha = 0) it
+// is folded into Ŝ and reset to 1.
 // ---------------------------------------------------------------------------------------------------
-template <int PER>
-__global__ __launch_bounds__(256) void prefill_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
-                                                      const float* __restrict__ ain, const float* __restrict__ bin,
-                                                      int H, int N, int d_k, int d_v, float* __restrict__ sctx_t,
-                                                      float* __restrict__ sctx_out) {
-  __shared__ float sk[2][256];
-  __shared__ float sv[2][256];
-  __shared__ float sab[2][2];
-  __shared__ float part_sum[256];
-  const int rh = blockIdx.x;
+namespace {
+constexpr int kPfT = 16;                 // tokens per staged block
+constexpr int kPfRows = 128;             // rows of S per workgroup
+constexpr int kPfThreads = 8 * kPfRows;  // 8 lanes per row
+constexpr float kPfRenorm = 0x1p-20f;
+}  // namespace
+
+// LDS per buffer: k [kPfT][d_kp], v [kPfT][kPfRows], alpha and beta [kPfT]
+inline size_t prefill_lds_bytes(int d_kp) { return 2 * (size_t)(kPfT * (d_kp + kPfRows + 2)) * sizeof(float); }
+
+template <int PER4>  // d_k padded to 32 * PER4 columns
+__global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __restrict__ kin,
+                                                             const float* __restrict__ vin,
+                                                             const float* __restrict__ ain,
+                                                             const float* __restrict__ bin, int H, int N, int d_k,
+                                                             int d_v, int nrb, float* __restrict__ sctx_t,
+                                                             float* __restrict__ sctx_out) {
+  extern __shared__ __align__(16) float pf_lds[];
+  constexpr int d_kp = 32 * PER4;
+  constexpr int buf_floats = kPfT * (d_kp + kPfRows + 2);
+  constexpr int kLd = (kPfT * d_kp + kPfThreads - 1) / kPfThreads;  // staged k elements per thread
+  constexpr int vLd = kPfT * kPfRows / kPfThreads;                  // staged v elements per thread
+  const int rh = blockIdx.x / nrb, rb = blockIdx.x - rh * nrb;
   const int r = rh / H, h = rh - r * H;
   const int tid = threadIdx.x;
-  const int nparts = 256 / d_v;
-  const int i = tid % d_v, part = tid / d_v;
-  const int d0 = part * PER;
-  float st[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) st[j] = 0.f;
+  const int row = tid >> 3, j = tid & 7;
+  const int i = rb * kPfRows + row;  // this lane's row of S (beyond d_v: computed on zeros, not stored)
+  const size_t tok0 = (size_t)r * N * H + h;  // token n of this (request, head): index tok0 + n * H
 
-  auto tok_k = [&](int n) { return kin + (((size_t)r * N + n) * H + h) * d_k; };
-  auto tok_v = [&](int n) { return vin + (((size_t)r * N + n) * H + h) * d_v; };
-  auto tok_s = [&](int n) { return ((size_t)r * N + n) * H + h; };
-  float nk = 0.f, nv = 0.f, na = 0.f, nb = 0.f;
-  if (N > 0) {
-    if (tid < d_k) nk = tok_k(0)[tid];
-    if (tid < d_v) nv = tok_v(0)[tid];
-    if (tid == 0) { na = ain[tok_s(0)]; nb = bin[tok_s(0)]; }
-  }
-  for (int n = 0; n < N; ++n) {
-    const int buf = n & 1;
-    if (tid < d_k) sk[buf][tid] = nk;
-    if (tid < d_v) sv[buf][tid] = nv;
-    if (tid == 0) { sab[buf][0] = na; sab[buf][1] = nb; }
-    __syncthreads();
-    if (n + 1 < N) {  // prefetch the next token while this one is processed
-      if (tid < d_k) nk = tok_k(n + 1)[tid];
-      if (tid < d_v) nv = tok_v(n + 1)[tid];
-      if (tid == 0) { na = ain[tok_s(n + 1)]; nb = bin[tok_s(n + 1)]; }
-    }
-    float p = 0.f;
-    if (part < nparts) {
+  float kr[kLd], vr[vLd], abr = 0.f;
+  auto fetch = [&](int blk) {  // block blk of tokens into registers (zeros past N, past d_k, past d_v)
 #pragma unroll
-      for (int j = 0; j < PER; ++j) p += st[j] * sk[buf][d0 + j];
+    for (int u = 0; u < kLd; ++u) {
+      const int x = tid + u * kPfThreads, tt = x / d_kp, c = x - tt * d_kp, n = blk * kPfT + tt;
+      kr[u] = (x < kPfT * d_kp && c < d_k && n < N) ? kin[(tok0 + (size_t)n * H) * d_k + c] : 0.f;
     }
-    part_sum[tid] = p;
-    __syncthreads();
-    if (part < nparts) {
-      float pi = 0.f;
-      for (int q = 0; q < nparts; ++q) pi += part_sum[q * d_v + i];
-      const float a = sab[buf][0], b = sab[buf][1];
-      const float u = b * (sv[buf][i] - a * pi);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) st[j] = a * st[j] + u * sk[buf][d0 + j];
+    for (int u = 0; u < vLd; ++u) {
+      const int x = tid + u * kPfThreads, tt = x / kPfRows, c = x - tt * kPfRows, n = blk * kPfT + tt;
+      const int iv = rb * kPfRows + c;
+      vr[u] = (iv < d_v && n < N) ? vin[(tok0 + (size_t)n * H) * d_v + iv] : 0.f;
     }
-    // part_sum is rewritten only after the next barrier; sk/sv/sab alternate buffers.
+    if (tid < 2 * kPfT) {
+      const int n = blk * kPfT + (tid >> 1);
+      abr = n < N ? ((tid & 1) ? bin : ain)[tok0 + (size_t)n * H] : 0.f;
+    }
+  };
+  auto stage = [&](int buf) {
+    float* base = pf_lds + buf * buf_floats;
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int x = tid + u * kPfThreads;
+      if (x < kPfT * d_kp) base[x] = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < vLd; ++u) base[kPfT * d_kp + tid + u * kPfThreads] = vr[u];
+    if (tid < 2 * kPfT) base[kPfT * (d_kp + kPfRows) + tid] = abr;  // (alpha, beta) pairs per token
+  };
+
+  float S[4 * PER4];
+#pragma unroll
+  for (int e = 0; e < 4 * PER4; ++e) S[e] = 0.f;
+  float g = 1.f;  // S = g * (the registers)
+  const int nblk = (N + kPfT - 1) / kPfT;
+  if (nblk > 0) {
+    fetch(0);
+    stage(0);
   }
-  if (part < nparts) {
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    if (blk + 1 < nblk) fetch(blk + 1);
+    const float* kb = pf_lds + buf * buf_floats;
+    const float* vb = kb + kPfT * d_kp;
+    const float* ab = vb + kPfT * kPfRows;
+    const int ntok = min(kPfT, N - blk * kPfT);
+    for (int tt = 0; tt < ntok; ++tt) {
+      f32x4_t kk[PER4];
+#pragma unroll
+      for (int m = 0; m < PER4; ++m) kk[m] = *reinterpret_cast<const f32x4_t*>(kb + tt * d_kp + 4 * (j + 8 * m));
+      const float vi = vb[tt * kPfRows + row];
+      const f32x2_t a_b = *reinterpret_cast<const f32x2_t*>(ab + 2 * tt);
+      f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < PER4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += S[4 * m + e] * kk[m][e];
+      float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      // sum over the row's 8 lanes: swap neighbours, swap pairs, mirror within the half row
+      dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0xB1, 0xF, 0xF, true));
+      dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x4E, 0xF, 0xF, true));
+      dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x141, 0xF, 0xF, true));
+      const float alpha = a_b.x, beta = a_b.y;
+      const float u = beta * (vi - alpha * (g * dot));
+      float gn = alpha * g;
+      if (gn < kPfRenorm) {  // the same decision in every lane (alpha and g are shared)
+#pragma unroll
+        for (int e = 0; e < 4 * PER4; ++e) S[e] *= gn;
+        gn = 1.f;
+      }
+      const float c = u * __builtin_amdgcn_rcpf(gn);
+#pragma unroll
+      for (int m = 0; m < PER4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[4 * m + e] += c * kk[m][e];
+      g = gn;
+    }
+    if (blk + 1 < nblk) stage(buf ^ 1);
+    __syncthreads();
+  }
+  if (i < d_v) {
     float* dst = sctx_t + (size_t)rh * d_k * d_v;
+    float* so = sctx_out ? sctx_out + ((size_t)rh * d_v + i) * d_k : nullptr;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) dst[(size_t)(d0 + j) * d_v + i] = st[j];
-    if (sctx_out) {
-      float* so = sctx_out + (size_t)rh * d_v * d_k + (size_t)i * d_k + d0;
+    for (int m = 0; m < PER4; ++m)
 #pragma unroll
-      for (int j = 0; j < PER; ++j) so[j] = st[j];
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int col = 4 * (j + 8 * m) + e;
+        if (col < d_k) {
+          const float x = g * S[4 * m + e];
+          dst[(size_t)col * d_v + i] = x;
+          if (so) so[col] = x;
+        }
+      }
   }
 }
 
-bool prefill_supported(int d_k, int d_v) {
-  if (d_v < 1 || d_v > 256 || 256 % d_v != 0) return false;
-  const int nparts = 256 / d_v;
-  if (d_k < 1 || d_k > 256 || d_k % nparts != 0) return false;
-  const int per = d_k / nparts;
-  return per <= 128 && (per & (per - 1)) == 0;
-}
+bool prefill_supported(int d_k, int d_v) { return d_k >= 1 && d_k <= 256 && d_v >= 1 && d_v <= 256; }
 
 hipError_t launch_prefill(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
                           int N, int d_k, int d_v, float* sctx_t, float* sctx_out, hipStream_t s) {
-  const int per = d_k / (256 / d_v);
-  dim3 grid(R * H), block(256);
+  const int per4 = (d_k + 31) / 32;
+  const int nrb = (d_v + kPfRows - 1) / kPfRows;
+  const size_t lds = prefill_lds_bytes(32 * per4);
+  dim3 grid((unsigned)((size_t)R * H * nrb)), block(kPfThreads);
 #define ONELA_PREFILL_CASE(P)                                                                                  \
   case P:                                                                                                      \
-    hipLaunchKernelGGL(prefill_kernel<P>, grid, block, 0, s, k, v, alpha, beta, H, N, d_k, d_v, sctx_t,       \
+    if (lds > 64 * 1024) {                                                                                     \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<P>),                   \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
+      if (e != hipSuccess) return e;                                                                           \
+    }                                                                                                          \
+    hipLaunchKernelGGL(prefill_kernel<P>, grid, block, lds, s, k, v, alpha, beta, H, N, d_k, d_v, nrb, sctx_t,  \
                        sctx_out);                                                                              \
     break;
-  switch (per) {
+  switch (per4) {
     ONELA_PREFILL_CASE(1)
     ONELA_PREFILL_CASE(2)
+    ONELA_PREFILL_CASE(3)
     ONELA_PREFILL_CASE(4)
+    ONELA_PREFILL_CASE(5)
+    ONELA_PREFILL_CASE(6)
+    ONELA_PREFILL_CASE(7)
     ONELA_PREFILL_CASE(8)
-    ONELA_PREFILL_CASE(16)
-    ONELA_PREFILL_CASE(32)
-    ONELA_PREFILL_CASE(64)
-    ONELA_PREFILL_CASE(128)
     default:
       return hipErrorInvalidValue;
   }

@@ -239,9 +239,7 @@ onela_status onela_prefill(onela_handle h, int32_t n_tokens, const float* d_k, c
   if (n_tokens > 0 && (!d_k || !d_v || !d_alpha || !d_beta))
     return fail(ONELA_ERR_INVALID_ARG, "prefill inputs must not be NULL");
   if (!prefill_supported(c.d_k, c.d_v))
-    return fail(ONELA_ERR_UNSUPPORTED,
-                "prefill needs 256 %% d_v == 0 and d_k / (256 / d_v) a power of two <= 128 (d_k=%d, d_v=%d)",
-                c.d_k, c.d_v);
+    return fail(ONELA_ERR_UNSUPPORTED, "prefill supports d_k, d_v <= 256 (d_k=%d, d_v=%d)", c.d_k, c.d_v);
   if ((double)c.num_requests * n_tokens * c.num_heads * (c.d_k > c.d_v ? c.d_k : c.d_v) > 9.0e15)
     return fail(ONELA_ERR_INVALID_ARG, "prompt too large");
   hipStream_t s = static_cast<hipStream_t>(stream);

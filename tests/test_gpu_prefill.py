@@ -1,0 +1,76 @@
+"""GPU prefill (onela_prefill) against the float64 oracle prefill: head sizes that are not multiples of the
+kernel's 32-column groups or 128-row workgroups, token counts that leave a ragged last block, no tokens,
+and decays small enough (or zero) to exercise the folding of the decay scale into the state."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_beam_amd import inputs, onela
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+
+
+def run_prefill(cfg, pf: inputs.PrefillInputs):
+    dev = gu.device()
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, 8, 2, qkv_dtype="f32", device=dev)
+    out = torch.full((cfg.R, cfg.H, cfg.d_v, cfg.d_k), float("nan"), dtype=torch.float32, device=dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    ctx.prefill(t(pf.k), t(pf.v), t(pf.alpha), t(pf.beta), sctx_out=out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    st = ctx.view()["sctx_t"].double().cpu().numpy()
+    ctx.close()
+    assert np.array_equal(st, np.swapaxes(got, -1, -2)), "installed S_ctx^T differs from the returned S_ctx"
+    return got
+
+
+def check(cfg, pf):
+    got = run_prefill(cfg, pf)
+    ref = oracle.prefill(pf.k, pf.v, pf.alpha, pf.beta)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    gu.log(f"  max|S err|={err:.3g} (max|S|={float(np.max(np.abs(ref))) if ref.size else 0.0:.3g})")
+    assert err < TOL
+    return got, ref
+
+
+@pytest.mark.parametrize("d_k,d_v,N", [
+    (128, 128, 100), (16, 16, 17), (64, 32, 1), (96, 200, 33), (256, 256, 40), (40, 7, 16), (1, 1, 5),
+    (200, 130, 31), (128, 256, 48),
+])
+def test_prefill_shapes(d_k, d_v, N):
+    cfg = inputs.config(2, R=2, H=3, d_k=d_k, d_v=d_v, prefill_steps=N)
+    gu.log(f"prefill d_k={d_k} d_v={d_v} N={N}")
+    check(cfg, inputs.prefill_inputs(cfg, seed=5))
+
+
+def test_prefill_no_tokens():
+    cfg = inputs.config(2, R=2, H=3, prefill_steps=0)
+    pf = inputs.prefill_inputs(cfg, steps=0)
+    got = run_prefill(cfg, pf)
+    assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("alpha_hi,zeros", [(0.3, False), (0.05, True), (1.0, True)])
+def test_prefill_small_and_zero_decay(alpha_hi, zeros):
+    """alpha ~ U(0, alpha_hi), optionally with exact zeros (a full reset of the state at that token)."""
+    cfg = inputs.config(2, R=2, H=4, prefill_steps=70)
+    pf = inputs.prefill_inputs(cfg, seed=6)
+    rng = np.random.default_rng(7)
+    pf.alpha = rng.uniform(0.0, alpha_hi, size=pf.alpha.shape).astype(np.float32)
+    if zeros:
+        pf.alpha[:, ::9] = 0.0
+    gu.log(f"prefill with alpha ~ U(0, {alpha_hi}) zeros={zeros}")
+    check(cfg, pf)
+
+
+def test_prefill_long_every_head():
+    """A 5120-token prompt on 4 heads: the decay scale is folded back many times."""
+    cfg = inputs.config(3, R=1, H=4)
+    gu.log(f"prefill {cfg.prefill_steps} tokens, R=1 H=4")
+    check(cfg, inputs.prefill_inputs(cfg, seed=8))
