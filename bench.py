@@ -387,6 +387,11 @@ def main():
                      "kernel_avg_us": kernel_avg_ms * 1e3, "kernel_us_by_decode_step": per_step_us,
                      "mfma_frac": mfma_flops / (kernel_ms.sum(axis=1).mean() * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
         "context_ms": context_ms,
+        # recurrent state kept per (beam, head) after the last step: a dense fp32 matrix (FullState) against the
+        # records appended along one chain (one per step: k in the input dtype, u fp32, alpha fp32)
+        "state_capacity": {"fullstate_bytes": cfg.d_v * cfg.d_k * 4,
+                           "records_bytes": cfg.L * (cfg.d_k * cfg.in_bytes + 4 * cfg.d_v + 4),
+                           "ratio": cfg.d_v * cfg.d_k * 4 / (cfg.L * (cfg.d_k * cfg.in_bytes + 4 * cfg.d_v + 4))},
     }
     if prefill_line is not None:
         line["prefill"] = prefill_line

@@ -104,7 +104,10 @@ typedef struct {
   int32_t slots;      /* record slots per (request, head) = max_beams * max_steps */
   int32_t fused;      /* 1 if steps run the fused bf16-MFMA kernel, 0 for the fp32-FMA kernel */
   void* rec_k;        /* REPLAY: [R][H][slots][d_k] in qkv_dtype (exact copies of the step's k) */
-  float* rec_u;       /* REPLAY: [R][H][slots][d_v] float32 */
+  float* rec_u;       /* REPLAY, float32.  fused = 0: [R][H][slots][d_v].  fused = 1: per (request, head) a
+                         block of S16 x D16 values (S16 = slots and D16 = d_v rounded up to multiples of 16) in
+                         16 x 16 tiles, so that the rows a wavefront appends for 16 beams are contiguous: the u
+                         of slot s, row i is at ((s / 16) * (D16 / 16) + i / 16) * 256 + (s % 16) * 16 + i % 16 */
   float* rec_alpha;   /* REPLAY: [R][H][slots] float32 (exact copies of the step's alpha) */
   int32_t* chains;    /* [max_steps][R][max_beams][max_steps]: the table after step t at index t-1 */
   float* sctx_t;      /* S_ctx transposed, [R][H][d_k][d_v] float32 */

@@ -22,6 +22,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits_rne(float x) {
   return u >> 16;
 }
 
+// Record u arena of one (request, head): blocks of 16 slots x 16 rows of u, 16 rows of one slot contiguous,
+// [slot / 16][row / 16][slot % 16][row % 16], so that the 16-beam x 16-row piece a wave of the fused kernel
+// appends is one contiguous kilobyte.  Slots are padded to a multiple of 16 and rows to d_v16, a multiple of 16.
+__host__ __device__ inline unsigned u_rows16(int d_v) { return ((unsigned)d_v + 15u) & ~15u; }
+__host__ __device__ inline unsigned u_slots16(int slots) { return ((unsigned)slots + 15u) & ~15u; }
+__host__ __device__ inline unsigned u_index(unsigned slot, unsigned row, unsigned d_v16) {
+  return (slot >> 4) * (16u * d_v16) + (row >> 4) * 256u + (slot & 15u) * 16u + (row & 15u);
+}
+
 // Loads of one element of q/k/v as float32, for either input dtype.
 __device__ __forceinline__ float load_in(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }

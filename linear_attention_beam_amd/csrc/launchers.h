@@ -18,7 +18,7 @@ struct StepArgs {
   const float* sctx_t;    // [R][H][d_k][d_v]
   const uint16_t* sctx_frag;  // bf16 high/low MFMA fragments of S_ctx (fused kernel only)
   void* rec_k;            // [R][H][slots][d_k] input dtype
-  float* rec_u;           // [R][H][slots][d_v]
+  float* rec_u;           // fused kernel: [R][H] tiles of u_slots16(slots) x u_rows16(d_v) (u_index); others [R][H][slots][d_v]
   float* rec_alpha;       // [R][H][slots]
   const int32_t* chain;   // chain table after this step, [R][B_max][L_max] (read by the generic kernel)
   // ancestry inputs (the fused kernel derives chains itself and writes the new table)

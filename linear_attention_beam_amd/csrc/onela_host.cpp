@@ -109,7 +109,9 @@ Layout make_layout(const onela_config* c) {
   l.decay = off;      off = align256(off + (l.fused ? 2 * R * H * B * (L + 1) * 4 : 0));
   if (c->mode == ONELA_MODE_REPLAY) {
     l.rec_k = off;     off = align256(off + R * H * slots * dk * in_bytes);
-    l.rec_u = off;     off = align256(off + R * H * slots * dv * 4);
+    // the fused kernel keeps u in 16 x 16 tiles of (slot, row), padded to multiples of 16; the others row by row
+    l.rec_u = off;     off = align256(off + (l.fused ? R * H * ((slots + 15) / 16 * 16) * ((dv + 15) / 16 * 16) * 4
+                                                     : R * H * slots * dv * 4));
     l.rec_alpha = off; off = align256(off + R * H * slots * 4);
     l.fullstate = 0;
   } else {

@@ -118,8 +118,10 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   // and write views never touch the same element.
   const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
   uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k) + arena * kDK;
-  const float* __restrict__ u_rd = a.rec_u + arena * d_v;
-  float* __restrict__ u_wr = a.rec_u + arena * d_v;
+  // u arena of this (request, head); d_v is a multiple of 32 here, so d_v16 = d_v
+  const size_t u_arena = (size_t)rh * u_slots16(a.slots) * d_v;
+  const float* __restrict__ u_rd = a.rec_u + u_arena;
+  float* __restrict__ u_wr = a.rec_u + u_arena;
   float* __restrict__ al_wr = a.rec_alpha + arena;
   auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
 
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         if (m0 + u < nch) {
-          const unsigned uo = (unsigned)slot_tab[bb * LS + m0 + u] * d_v + dv0;
+          const unsigned uo = u_index((unsigned)slot_tab[bb * LS + m0 + u], (unsigned)dv0, (unsigned)d_v);
           U[u] = *reinterpret_cast<const f32x4_t*>(u_rd + uo);
         }
       }
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
         u4[e] = uu;
         o4[e] = al * sq[e] + kq * uu;
       }
-      *reinterpret_cast<f32x4_t*>(u_wr + (own * d_v + dv0)) = u4;
+      *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
       *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
     }
   }

@@ -48,7 +48,9 @@ def expected_bytes(c):
     total += up(2 * R * H * B * (L + 1) * 4 if fused else 0)
     if c.mode == onela.ONELA_MODE_REPLAY:
         slots = B * L
-        total += up(R * H * slots * dk * s_in) + up(R * H * slots * dv * 4) + up(R * H * slots * 4)
+        pad16 = lambda x: (x + 15) // 16 * 16  # noqa: E731  (u records: 16 x 16 blocks of slots x rows)
+        u_elems = pad16(slots) * pad16(dv) if fused else slots * dv
+        total += up(R * H * slots * dk * s_in) + up(R * H * u_elems * 4) + up(R * H * slots * 4)
     else:
         total += up(2 * R * H * B * dk * dv * 4)
     return total
@@ -57,7 +59,7 @@ def expected_bytes(c):
 @pytest.mark.parametrize("kw", [
     {}, dict(d_v=256), dict(qkv_dtype=onela.ONELA_F32, d_k=16, d_v=16), dict(mode=onela.ONELA_MODE_FULLSTATE),
     dict(flags=onela.ONELA_FLAG_FORCE_GENERIC), dict(flags=onela.ONELA_FLAG_MATERIALIZE), dict(d_k=64, d_v=100),
-    dict(max_steps=64, max_beams=1),
+    dict(max_steps=64, max_beams=1), dict(max_steps=3, max_beams=5, d_v=7), dict(max_steps=3, max_beams=5, d_v=96),
 ])
 def test_workspace_size(kw):
     c = cfg(**kw)
@@ -99,3 +101,17 @@ def test_beam_select_bad_args(args, status):
     with pytest.raises(onela.OnelaError) as e:
         onela.onela_beam_select_scratch(*args)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("slots,d_v", [(32, 128), (20, 7), (1, 1), (48, 256)])
+def test_u_record_tiling(slots, d_v):
+    """The binding's untiling of the u arena follows the tile formula documented for onela_view.rec_u."""
+    import torch
+    S16, D16 = onela.pad16(slots), onela.pad16(d_v)
+    flat = torch.full((2, 3, S16 * D16), -1.0, dtype=torch.float64)
+    for s in range(slots):
+        for i in range(d_v):
+            flat[:, :, ((s // 16) * (D16 // 16) + i // 16) * 256 + (s % 16) * 16 + i % 16] = s * 1000 + i
+    got = onela.unblock_u(flat, slots, d_v)
+    want = torch.arange(slots, dtype=torch.float64)[:, None] * 1000 + torch.arange(d_v, dtype=torch.float64)
+    assert torch.equal(got, want.expand(2, 3, slots, d_v))
