@@ -37,6 +37,7 @@ def assert_same(si, n_beams, got):
     (4, 512, 256, 2048, False),  # the largest n_beams
     (3, 300, 50, 700, True),    # many exact ties: the flat-index order decides
     (1, 1, 9000, 1, True),
+    (2, 8193, 1, 7, False),     # one candidate per beam, just over one chunk
 ])
 def test_select_matches_oracle(R, n_prev, n_cand, n_beams, ties):
     gu.log(f"select R={R} n_prev={n_prev} n_cand={n_cand} n_beams={n_beams} ties={ties}")
@@ -121,3 +122,18 @@ def test_select_feeds_decode():
             for t0 in range(cfg.L):
                 assert np.array_equal(view["chains"][t0, r].cpu().numpy(), chains[t0]), (r, t0)
     ctx.close()
+
+
+def test_select_all_equal_scores():
+    """Every candidate of a request scores the same: the flat index alone orders them, so the first flat
+    indices survive; then one candidate above a 20000-way tie."""
+    gu.log("select with every score equal")
+    si = inputs.SelectInputs(np.zeros((2, 40), np.float32), np.zeros((2, 40, 500), np.float32))
+    got = run_select(si, 300)
+    assert_same(si, 300, got)
+    assert np.array_equal(got[0][0], np.arange(300) // 500) and np.array_equal(got[1][0], np.arange(300) % 500)
+    si = inputs.SelectInputs(np.zeros((1, 40), np.float32), np.full((1, 40, 500), -1.5, np.float32))
+    si.logp[0, 39, 499] = -1.0
+    got = run_select(si, 2048)
+    assert_same(si, 2048, got)
+    assert got[0][0, 0] == 39 and got[1][0, 0] == 499
