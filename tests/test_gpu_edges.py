@@ -67,6 +67,19 @@ def test_ragged_beams(d_v, tile, generic):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
 
 
+@pytest.mark.parametrize("d_v,tile", [(128, 16), (96, 32), (224, 64), (32, 0)])
+def test_odd_record_capacity(d_v, tile):
+    """max_beams = 37: the slots of a (request, head) are not a multiple of 16, so the fused kernel's last
+    16-slot tile of u records is partial (the arena is padded); every head and record checked."""
+    cfg = inputs.config(2, R=2, H=3, d_v=d_v, B=37, L=3)
+    gu.log(f"odd record capacity: B=37 L=3 d_v={d_v} tile={tile}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile)
+    assert run.view["fused"] and run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
 def test_tiles_and_xcd_mapping_agree():
     """R*H = 16 (a multiple of 8, XCD-grouped mapping) and every tile size give the same outputs."""
     cfg = inputs.config(2, R=2, H=8, B=96, L=3)
