@@ -211,3 +211,38 @@ def test_materializing_replay(d_k, d_v, dtype):
     assert not run.view["fused"]
     assert run.status == onela.ONELA_OK
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_single_beam_is_sequential_gdn(generic):
+    """One beam for 24 steps is plain sequential GDN from S_ctx: compared with the oracle's sequential
+    recurrence (the dense update, no records or chains)."""
+    cfg = inputs.config(1, R=2, H=3, B=1, L=24)
+    gu.log(f"single beam, 24 steps, generic={generic}")
+    steps = inputs.decode_inputs(cfg)
+    for s in steps:
+        s.parent[:] = 0
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, force_generic=generic)
+    worst = 0.0
+    for r in range(cfg.R):
+        for h in range(cfg.H):
+            f = lambda name: np.stack([gu._f32(s, name, r, h)[0] for s in steps])  # noqa: E731
+            ref = oracle.sequential_outputs(sctx[r, h], f("q"), f("k"), f("v"),
+                                            np.array([s.alpha[r, 0, h] for s in steps]),
+                                            np.array([s.beta[r, 0, h] for s in steps]))
+            got = np.stack([run.head_o(t, r, h)[0] for t in range(cfg.L)])
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+    gu.log(f"  max|o err|={worst:.3g}")
+    assert worst <= gu.TOL
+
+
+def test_many_beams():
+    """8192 beams per request (128 tiles of 64 per (request, head)), Zipf(1.1) parents, every head."""
+    cfg = inputs.config(2, R=1, H=2, B=8192, L=3)
+    gu.log("8192 beams, R=1 H=2 L=3")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx)
+    assert run.view["fused"] and run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
