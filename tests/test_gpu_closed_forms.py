@@ -10,6 +10,7 @@
   relabelling                  permuting the new beams of a step (and remapping the next step's parents)
                                permutes that step's outputs and leaves the later ones unchanged, bit for bit
   duplicates                   two beams with the same parent and inputs get the same output, bit for bit
+  alpha = 0                    the step forgets S_ctx and the whole history: o_t = beta (k_t . q_t) v_t
 """
 
 import numpy as np
@@ -199,3 +200,22 @@ def test_relabelling_and_duplicates(variant):
     assert np.array_equal(p[1], a[1][:, inv]), "relabelled step"
     for t in range(2, L):
         assert np.array_equal(p[t], a[t]), f"step {t + 1} after the relabelled one"
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_alpha_zero(variant):
+    """alpha = 0 forgets everything before the step: S_t = beta v k^T, so o_t = beta (k . q) v for every beam,
+    whatever S_ctx and the history hold (all decay products along the chains are 0)."""
+    gu.log(f"closed form alpha = 0: {variant}")
+    rng = np.random.default_rng(505)
+    dtype = VARIANTS[variant][0]
+    sctx = rng.standard_normal((R, H, D, D)).astype(np.float32)
+    steps = make_steps(rng, dtype, alpha=0.0)
+    outs, _ = run(variant, sctx, steps)
+    worst = 0.0
+    for t, s in enumerate(steps):
+        q, k, v = (dec(x, dtype).astype(np.float64) for x in (s.q, s.k, s.v))
+        ex = s.beta[..., None].astype(np.float64) * np.sum(k * q, axis=-1, keepdims=True) * v
+        worst = max(worst, float(np.max(np.abs(outs[t] - ex))))
+    gu.log(f"  max|o - closed form| = {worst:.3g}")
+    assert worst < 1e-3
