@@ -15,14 +15,21 @@
 //            parent's row (chain entries and A in one round trip), and writes its own (c_j alpha_b for the
 //            parent's records, 1 for its own record, A alpha_b) for the next step, so no record alpha is
 //            gathered.
-//   Phase 1  (16 lanes per (beam, chain record)) dot products of the chain keys with k and q, and k . q,
-//            reduced with DPP inside a 16-lane row; append the record key and alpha.
-//   Phase 2  for 16 beams at a time, v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over
-//            d_k, high then low half into one float32 accumulator.  In the accumulator lane l holds beam
-//            l % 16 and d_v rows 4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on
-//            16-byte pieces: one float4 load of each chain record's u, float4 stores of u and o:
+//   Phase 1  the u of the chain records (this lane's 4-row piece of each of its 4 beams) starts streaming
+//            into a register ring; then 16 lanes per (beam, chain record) take the dot products of the chain
+//            keys with k and q (a ring of kD1 keys per lane), and k . q, reduced with DPP inside a 16-lane
+//            row; append the record key and alpha.
+//   Phase 2  the replay: sum_j c_j (K_j.k) U_j and sum_j c_j (K_j.q) U_j for the 4 beams of this lane,
+//            records-major over a ring of kRM records x 4 tiles.  Then for 16 beams at a time,
+//            v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over d_k, high then low half
+//            into one float32 accumulator.  In the accumulator lane l holds beam l % 16 and d_v rows
+//            4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on 16-byte pieces (one
+//            float4 load of each chain record's u) and u and o leave as float4 stores:
 //              p = A P_k + sum_j c_j (K_j.k) U_j,  u = beta (v - alpha p),
 //              o = alpha (A P_q + sum_j c_j (K_j.q) U_j) + (k.q) u.
+//   Every gather of phases 1 and 2 is an unconditional load in a software pipeline (indices past the end
+//   are clamped to a valid record and the values dropped): the compiler's waits on the in-order vmcnt then
+//   cover exactly the load consumed, not the loads and stores issued after it.
 // Workgroups of one (request, head) are mapped to the same XCD (dispatch is round-robin over the 8 XCDs)
 // so their S_ctx reads share one L2.
 #include "device_common.h"
@@ -34,8 +41,13 @@ namespace {
 constexpr int kDK = 128;             // d_k of the fused kernel
 constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
-constexpr int kItems = 4;            // chain keys in flight per 16-lane group (phase 1)
-constexpr int kChunk = 4;            // chain records in flight per beam (phase 2)
+constexpr int kD1 = 4;               // chain keys in flight per lane (phase 1)
+constexpr int kRM = 2;               // chain records per tile in flight per lane (phase 2)
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 constexpr int kPX = 4;               // 16-byte pieces of the k and q rows per thread held in registers
 constexpr int kPV = 2;               // 16-byte pieces of the v rows per thread held in registers
 
@@ -271,128 +283,163 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
   }
   __syncthreads();
 
-  // ---- phase 2 gathers.  The chain records' u (kChunk at a time, this lane's 4-row piece) is gathered per
-  // beam tile, the first tile's during phase 1 and each next tile's during the current tile's stores and
-  // MFMAs.  Only records that exist are loaded, so a short chain issues no redundant requests.
-  f32x4_t U[kChunk];
-  auto gather = [&](int mt, int m0) {
-    const int bb = min(mt * 16 + col, nb - 1);
-    if (nch > 0) {
+  // ---- after the chain tables: every remaining global load is a gather whose address comes from LDS.  The
+  // gathers run as software pipelines of unconditional loads (indices past the end are clamped to a valid
+  // record and their values dropped), so that the compiler's in-order vmcnt waits cover exactly the load
+  // being consumed and never the ones issued after it.
+  const int g16 = tid >> 4, j16 = tid & 15;
+  const int ngroups = nthreads >> 4;
+  auto rest = [&](auto rm_c) {
+    constexpr int RM = decltype(rm_c)::value;  // chain records per tile in flight in the u ring (0: no chain)
+    constexpr int NU = RM > 0 ? RM * kTiles : 1;
+    int bcs[kTiles];  // this lane's beam in each 16-beam tile, clamped to the tile's last beam
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        if (m0 + u < nch) {
-          const unsigned uo = u_index((unsigned)slot_tab[bb * LS + m0 + u], (unsigned)dv0, (unsigned)d_v);
-          U[u] = *reinterpret_cast<const f32x4_t*>(u_rd + uo);
-        }
-      }
+    for (int mt = 0; mt < kTiles; ++mt) bcs[mt] = min(mt * 16 + col, nb - 1);
+    auto u_load = [&](int mt, int m) -> f32x4_t {
+      const unsigned uo = u_index((unsigned)slot_tab[bcs[mt] * LS + m], (unsigned)dv0, (unsigned)d_v);
+      return *reinterpret_cast<const f32x4_t*>(u_rd + uo);
+    };
+    // u ring, records-major: U[r * kTiles + mt] holds record m0 + r of tile mt.  Its first RM records go out
+    // now and land during phase 1.
+    f32x4_t U[NU];
+    if constexpr (RM > 0) {
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int mt = 0; mt < kTiles; ++mt) U[r * kTiles + mt] = u_load(mt, min(r, nch - 1));
     }
-  };
-  gather(0, 0);
 
-  // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q; then k . q; append k, alpha ----
-  {
-    const int g = tid >> 4, j = tid & 15;
-    const int ngroups = nthreads >> 4;
-    const int items = nb * nch;
-    for (int it0 = g * kItems; it0 < items; it0 += ngroups * kItems) {
-      u32x4_t K[kItems];
-      int2 it[kItems];
-#pragma unroll
-      for (int u = 0; u < kItems; ++u) {
-        if (it0 + u < items) {
-          it[u] = item_tab[it0 + u];
-          K[u] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)it[u].x * kDK + j * 8));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kItems; ++u) {
-        if (it0 + u < items) {  // uniform over the 16 lanes of the group
-          const int pos = it[u].y & 0xFFFF, bb = it[u].y >> 16;
-          const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
-          const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
-          const float dk = row16_sum(dot8_bf16(K[u], kx));
-          const float dq = row16_sum(dot8_bf16(K[u], qx));
-          if (j == 0) {
+    // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q into the coefficient table.  Group g
+    // takes items g, g + ngroups, ...; a ring of kD1 chain keys per lane. ----
+    if constexpr (RM > 0) {
+      const int items = nb * nch;
+      const int kmax = (items + ngroups - 1) / ngroups;
+      u32x4_t K[kD1];
+      int IY[kD1];
+      auto k_load = [&](int kk, int d) {
+        const int2 e = item_tab[min(kk * ngroups + g16, items - 1)];
+        IY[d] = e.y;
+        K[d] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)e.x * kDK + j16 * 8));
+      };
+      auto k_use = [&](int kk, int d) {
+        if (kk * ngroups + g16 < items) {  // uniform over the 16 lanes of the group
+          const int pos = IY[d] & 0xFFFF, bb = IY[d] >> 16;
+          const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
+          const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
+          const float dk = row16_sum(dot8_bf16(K[d], kx));
+          const float dq = row16_sum(dot8_bf16(K[d], qx));
+          if (j16 == 0) {
             const float c = c_tab[pos];
             coef[pos] = (f32x2_t){c * dk, c * dq};
           }
         }
+      };
+#pragma unroll
+      for (int d = 0; d < kD1; ++d) k_load(d, d);
+      int k0 = 0;
+      for (; k0 + kD1 < kmax; k0 += kD1) {
+#pragma unroll
+        for (int d = 0; d < kD1; ++d) {
+          k_use(k0 + d, d);
+          k_load(k0 + kD1 + d, d);
+        }
       }
+#pragma unroll
+      for (int d = 0; d < kD1; ++d) k_use(k0 + d, d);
     }
-    for (int bb = g; bb < nb; bb += ngroups) {
-      const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j * 16);
-      const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j * 16);
+    // k . q of every beam; append the record key and alpha
+    for (int bb = g16; bb < nb; bb += ngroups) {
+      const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
+      const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
       const float kq = row16_sum(dot8_bf16(kx, qx));
       const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-      *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j * 8)) = kx;
-      if (j == 0) {
+      *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j16 * 8)) = kx;
+      if (j16 == 0) {
         beamKq[bb] = kq;
         al_wr[own] = beamAl[bb];
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- phase 2: MFMA contraction + replay + append, 16 beams per iteration ----
+    // ---- phase 2: the replay over the u ring (sums per tile in P, Q), then per tile the MFMA contraction,
+    // u and o ----
+    floatx4_t P[kTiles], Q[kTiles];
 #pragma unroll
-  for (int mt = 0; mt < kTiles; ++mt) {
-    if (mt * 16 >= nb) break;
-    const int bb = mt * 16 + col;  // this lane's beam
-    floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-    // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const bf16x8_t bk =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
-      const bf16x8_t bq = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
-        pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
-      }
+    for (int mt = 0; mt < kTiles; ++mt) {
+      P[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      Q[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
     }
-    const int bc = min(bb, nb - 1);
-    const float A = beamA[bc];
-    float p[4], sq[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = A * pk[e];
-      sq[e] = A * pq[e];
-    }
-    const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bc * lay.vrow + dv0 * 2);
-    for (int m0 = 0; m0 < nch; m0 += kChunk) {
-      if (m0 > 0) gather(mt, m0);
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        if (m0 + u < nch) {
-          const f32x2_t c = coef[bc * LS + m0 + u];
+    if constexpr (RM > 0) {
+      auto acc = [&](int mt, int m, int i) {
+        if (mt * 16 < nb) {
+          const f32x2_t c = coef[bcs[mt] * LS + m];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p[e] += c.x * U[u][e];
-            sq[e] += c.y * U[u][e];
+            P[mt][e] += c.x * U[i][e];
+            Q[mt][e] += c.y * U[i][e];
           }
         }
-      }
-    }
-    if ((mt + 1) * 16 < nb) gather(mt + 1, 0);  // next tile's loads fly during these stores and its MFMAs
-    if (bb < nb) {
-      const float al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
-      const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-      const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
-      const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
-                           bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
-      f32x4_t u4, o4;
+      };
+      int m0 = 0;
+      for (; m0 + RM < nch; m0 += RM) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float uu = be * (v4[e] - al * p[e]);
-        u4[e] = uu;
-        o4[e] = al * sq[e] + kq * uu;
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+          for (int mt = 0; mt < kTiles; ++mt) {
+            acc(mt, m0 + r, r * kTiles + mt);
+            U[r * kTiles + mt] = u_load(mt, min(m0 + RM + r, nch - 1));
+          }
       }
-      *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
-      *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+        if (m0 + r < nch) {
+#pragma unroll
+          for (int mt = 0; mt < kTiles; ++mt) acc(mt, m0 + r, r * kTiles + mt);
+        }
     }
-  }
+#pragma unroll
+    for (int mt = 0; mt < kTiles; ++mt) {
+      if (mt * 16 >= nb) break;
+      const int bb = mt * 16 + col;
+      floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8_t bk = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
+        const bf16x8_t bq = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+          pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
+          pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
+        }
+      }
+      if (bb < nb) {
+        const float A = beamA[bb], al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
+        const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
+        const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bb * lay.vrow + dv0 * 2);
+        const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
+        const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
+                             bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
+        f32x4_t u4, o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float uu = be * (v4[e] - al * (A * pk[e] + P[mt][e]));
+          u4[e] = uu;
+          o4[e] = al * (A * pq[e] + Q[mt][e]) + kq * uu;
+        }
+        *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
+        *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
+      }
+    }
+  };
+  if (nch == 0)
+    rest(IntC<0>{});
+  else if (nch == 1)
+    rest(IntC<1>{});
+  else
+    rest(IntC<(NB >= 128 ? 1 : kRM)>{});  // 8 tiles per lane: one record per tile in flight
 }
 
 bool fused_supported(int d_k, int d_v, int L_max) {
