@@ -2,7 +2,8 @@
 // state, record replay and record append in one kernel ("Scientific Impact Assessment: OneLA", §1: a fused
 // GPU kernel reuses S_ctx across beams; paper index page, Abstract).
 //
-// Workgroup = (request, head, tile of NB beams); d_v / 16 waves of 64 lanes (d_k = 128 fixed).
+// Workgroup = (request, head, tile of NB beams), or a run of consecutive tiles of one (request, head) when
+// the register file admits a single workgroup per CU; d_v / 16 waves of 64 lanes (d_k = 128 fixed).
 //   Phase 0  everything that needs nothing from the ancestry goes out in the first round trip: parents,
 //            alpha and beta; k, q and v rows of the tile (16-byte loads, held in registers and written to
 //            LDS only after the chain rows are requested, so that the two round trips overlap); this
@@ -32,6 +33,8 @@
 //   cover exactly the load consumed, not the loads and stores issued after it.
 // Workgroups of one (request, head) are mapped to the same XCD (dispatch is round-robin over the 8 XCDs)
 // so their S_ctx reads share one L2.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -43,6 +46,7 @@ constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
 constexpr int kD1 = 4;               // chain keys in flight per lane (phase 1)
 constexpr int kRM = 2;               // chain records per tile in flight per lane (phase 2)
+constexpr int kPersistTiles = 4;     // tiles per workgroup when one workgroup fills a CU
 
 template <int V>
 struct IntC {
@@ -82,120 +86,34 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L, int d_v) {
 inline size_t lds_budget(int d_v) { return (size_t)640 * d_v; }
 }  // namespace
 
-template <int NB>
-__global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile) {
+template <int NB, bool PERSIST>
+__global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile, int tps) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
   const int LS = table_stride(L);
   const FusedLds lay = fused_layout(NB, L, d_v);
-  unsigned char* xs = lds + lay.xs;
-  unsigned char* vs = lds + lay.vs;
-  int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
-  float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
-  f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
-  int2* item_tab = reinterpret_cast<int2*>(lds + lay.item);
-  float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
-  float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
-  float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
-  float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
-  int* beamPar = reinterpret_cast<int*>(lds + lay.beamPar);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
 
-  // ---- workgroup -> (request, head, tile); tiles of one (request, head) share an XCD ----
-  const int G = a.R * H;
-  int rh, tile;
-  if ((G & 7) == 0) {
+  // ---- workgroup -> (request, head, run of tps consecutive tiles); workgroups of one (request, head) share
+  // an XCD ----
+  const int nsplit = (ntile + tps - 1) / tps;
+  int rh, split;
+  if (((a.R * H) & 7) == 0) {
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    rh = (j / ntile) * 8 + x;
-    tile = j - (j / ntile) * ntile;
+    rh = (j / nsplit) * 8 + x;
+    split = j - (j / nsplit) * nsplit;
   } else {
-    rh = blockIdx.x / ntile;
-    tile = blockIdx.x - rh * ntile;
+    rh = blockIdx.x / nsplit;
+    split = blockIdx.x - rh * nsplit;
   }
   const int r = rh / H, h = rh - r * H;
-  const int b0 = tile * NB;
-  const int nb = min(NB, n - b0);
   const int nch = a.t - 1;
   const size_t arena = (size_t)rh * a.slots;
-  // Uniform per-workgroup bases; per-lane offsets are 32-bit (the host checks that they fit).
-  const size_t row0 = ((size_t)r * n + b0) * H + h;  // input row of beam b0 at this head
-  const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q) + row0 * kDK;
-  const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k) + row0 * kDK;
-  const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v) + row0 * d_v;
-  float* __restrict__ o_wr = a.o + row0 * d_v;
-  const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs
-  // Records are read only at slots of earlier steps and written only at this step's slots, so the read
-  // and write views never touch the same element.
-  const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
-  uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k) + arena * kDK;
-  // u arena of this (request, head); d_v is a multiple of 32 here, so d_v16 = d_v
-  const size_t u_arena = (size_t)rh * u_slots16(a.slots) * d_v;
-  const float* __restrict__ u_rd = a.rec_u + u_arena;
-  float* __restrict__ u_wr = a.rec_u + u_arena;
-  float* __restrict__ al_wr = a.rec_alpha + arena;
-  auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
-
-  // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers.  Every load
-  // goes out before the first value is used: thread tid < NB keeps beam tid's parent, alpha and beta in
-  // registers until the k, q, v and S_ctx requests have been issued (nthreads = 4 d_v >= NB). ----
-  // loads are issued unconditionally (clamped indices, values dropped afterwards) so that the compiler can
-  // count them exactly and later waits do not cover loads issued after the one they need
-  const int tb = min(tid, nb - 1);
-  int pP = a.parent[(size_t)r * n + b0 + tb];
-  float pAl = a.alpha[in_row(tb)];
-  float pBe = a.beta[in_row(tb)];
-  __builtin_amdgcn_sched_barrier(0);  // keep these first in issue order
-  // k, q and v of the tile go to registers now and to LDS only after the chain rows are requested, so
-  // the chain round trip overlaps this one
-  const int vc = d_v >> 3;  // 16-byte pieces per v row
-  auto x_piece = [&](int idx) -> u32x4_t {  // idx < NB * 32; rows < NB are keys, the others queries
-    const int row = idx >> 4, c = idx & 15;
-    const int bb = row < NB ? row : row - NB;
-    u32x4_t val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)min(bb, nb - 1) * hk + c * 8);
-    if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
-    return val;
-  };
-  auto v_piece = [&](int idx) -> u32x4_t {  // idx < NB * vc
-    const int bb = idx / vc, c = idx - bb * vc;
-    u32x4_t val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)min(bb, nb - 1) * hv + c * 8);
-    if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
-    return val;
-  };
-  u32x4_t XR[kPX], VR[kPV];
-#pragma unroll
-  for (int u = 0; u < kPX; ++u) XR[u] = x_piece(min(tid + u * nthreads, NB * 32 - 1));
-#pragma unroll
-  for (int u = 0; u < kPV; ++u) VR[u] = v_piece(min(tid + u * nthreads, NB * vc - 1));
-  auto store_x = [&]() {
-#pragma unroll
-    for (int u = 0; u < kPX; ++u) {
-      const int idx = tid + u * nthreads;
-      if (idx < NB * 32) *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = XR[u];
-    }
-    for (int idx = tid + kPX * nthreads; idx < NB * 32; idx += nthreads)
-      *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = x_piece(idx);
-#pragma unroll
-    for (int u = 0; u < kPV; ++u) {
-      const int idx = tid + u * nthreads;
-      if (idx < NB * vc) {
-        const int bb = idx / vc;
-        *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = VR[u];
-      }
-    }
-    for (int idx = tid + kPV * nthreads; idx < NB * vc; idx += nthreads) {
-      const int bb = idx / vc;
-      *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = v_piece(idx);
-    }
-  };
-  const int gq = lane >> 4, col = lane & 15;
-  const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
-  constexpr int kTiles = NB / 16;
-  // fragment file per (request, head): [hl][w][ks][mi][lane][8], rows 32 w + 16 mi + lane % 16; wave x
-  // takes the block w = x / 2, mi = x % 2
+  // S_ctx rows of a wave.  Fragment file per (request, head): [hl][w][ks][mi][lane][8], rows
+  // 32 w + 16 mi + lane % 16; wave x takes the block w = x / 2, mi = x % 2.  Wave w owns d_v rows
+  // 16w .. 16w+15; their bf16 high and low halves stay in registers while the workgroup runs.
   bf16x8_t sf[kKS][2];
-  {
+  auto load_sf = [&](int wave, int lane) {
     const int W = d_v / 32;
     const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
     const u32x4_t* __restrict__ fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
@@ -205,241 +123,348 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile)
       for (int hl = 0; hl < 2; ++hl)
         sf[ks][hl] = __builtin_bit_cast(
             bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every streaming request is out before the parents are consumed
-  if (tid >= nb) {
-    pP = 0;
-    pAl = 0.f;
-    pBe = 0.f;
-  }
-  if (tid < NB) {
-    if (tid < nb && (pP < 0 || pP >= a.b_prev)) {  // sticky flag; decode as a child of beam 0 so accesses stay in bounds
-      *a.flag = a.epoch;
-      pP = 0;
-    }
-    beamPar[tid] = pP;
-    beamAl[tid] = pAl;
-    beamBe[tid] = pBe;
-  }
-  __syncthreads();
-
-  // ---- phase 0 (cont.): the parents' chain rows and decay rows in one round trip; this step's rows ----
-  const int drow = L + 1;    // decay row: c_0 .. c_{L-1}, then A
-  const int nper = nch + 1;  // per beam: nch chain entries, then the parent's total decay A
-  int raw[4];
-  float dec[4];
-  auto chain_load = [&](int base) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * nthreads + tid;
-      raw[u] = 0;
-      dec[u] = 1.f;
-      if (idx < nb * nper) {
-        const int bb = idx / nper, m = idx - bb * nper;
-        if (m < nch) {
-          raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
-          dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
-        } else if (nch > 0) {
-          dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L];
-        }
-      }
-    }
   };
-  chain_load(0);
-  store_x();
-  for (int base = 0; base < nb * nper; base += 4 * nthreads) {
-    if (base > 0) chain_load(base);
+
+  auto do_tile = [&](const int tile, const int tid) {
+    unsigned char* xs = lds + lay.xs;
+    unsigned char* vs = lds + lay.vs;
+    int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
+    float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
+    f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
+    int2* item_tab = reinterpret_cast<int2*>(lds + lay.item);
+    float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
+    float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
+    float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
+    float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
+    int* beamPar = reinterpret_cast<int*>(lds + lay.beamPar);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int b0 = tile * NB;
+    const int nb = min(NB, n - b0);
+    // Uniform per-workgroup bases; per-lane offsets are 32-bit (the host checks that they fit).
+    const size_t row0 = ((size_t)r * n + b0) * H + h;  // input row of beam b0 at this head
+    const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q) + row0 * kDK;
+    const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k) + row0 * kDK;
+    const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v) + row0 * d_v;
+    float* __restrict__ o_wr = a.o + row0 * d_v;
+    const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs
+    // Records are read only at slots of earlier steps and written only at this step's slots, so the read
+    // and write views never touch the same element.
+    const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
+    uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k) + arena * kDK;
+    // u arena of this (request, head); d_v is a multiple of 32 here, so d_v16 = d_v
+    const size_t u_arena = (size_t)rh * u_slots16(a.slots) * d_v;
+    const float* __restrict__ u_rd = a.rec_u + u_arena;
+    float* __restrict__ u_wr = a.rec_u + u_arena;
+    float* __restrict__ al_wr = a.rec_alpha + arena;
+    auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
+
+    // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers.  Every load
+    // goes out before the first value is used: thread tid < NB keeps beam tid's parent, alpha and beta in
+    // registers until the k, q, v and S_ctx requests have been issued (nthreads = 4 d_v >= NB). ----
+    // loads are issued unconditionally (clamped indices, values dropped afterwards) so that the compiler can
+    // count them exactly and later waits do not cover loads issued after the one they need
+    const int tb = min(tid, nb - 1);
+    int pP = a.parent[(size_t)r * n + b0 + tb];
+    float pAl = a.alpha[in_row(tb)];
+    float pBe = a.beta[in_row(tb)];
+    __builtin_amdgcn_sched_barrier(0);  // keep these first in issue order
+    // k, q and v of the tile go to registers now and to LDS only after the chain rows are requested, so
+    // the chain round trip overlaps this one
+    const int vc = d_v >> 3;  // 16-byte pieces per v row
+    auto x_piece = [&](int idx) -> u32x4_t {  // idx < NB * 32; rows < NB are keys, the others queries
+      const int row = idx >> 4, c = idx & 15;
+      const int bb = row < NB ? row : row - NB;
+      u32x4_t val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)min(bb, nb - 1) * hk + c * 8);
+      if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
+      return val;
+    };
+    auto v_piece = [&](int idx) -> u32x4_t {  // idx < NB * vc
+      const int bb = idx / vc, c = idx - bb * vc;
+      u32x4_t val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)min(bb, nb - 1) * hv + c * 8);
+      if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
+      return val;
+    };
+    u32x4_t XR[kPX], VR[kPV];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * nthreads + tid;
-      if (idx < nb * nper) {
-        const int bb = idx / nper, m = idx - bb * nper;
-        float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
-        if (m < nch) {
-          const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
-          slot_tab[bb * LS + m] = sl;
-          c_tab[bb * LS + m] = dec[u];
-          item_tab[bb * nch + m] = make_int2(sl, (bb << 16) | (bb * LS + m));
-          dout[m] = dec[u] * beamAl[bb];
-          if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
-        } else {
-          dout[nch] = 1.f;
-          dout[L] = dec[u] * beamAl[bb];
-          beamA[bb] = dec[u];
+    for (int u = 0; u < kPX; ++u) XR[u] = x_piece(min(tid + u * nthreads, NB * 32 - 1));
+#pragma unroll
+    for (int u = 0; u < kPV; ++u) VR[u] = v_piece(min(tid + u * nthreads, NB * vc - 1));
+    auto store_x = [&]() {
+#pragma unroll
+      for (int u = 0; u < kPX; ++u) {
+        const int idx = tid + u * nthreads;
+        if (idx < NB * 32) *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = XR[u];
+      }
+      for (int idx = tid + kPX * nthreads; idx < NB * 32; idx += nthreads)
+        *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = x_piece(idx);
+#pragma unroll
+      for (int u = 0; u < kPV; ++u) {
+        const int idx = tid + u * nthreads;
+        if (idx < NB * vc) {
+          const int bb = idx / vc;
+          *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = VR[u];
         }
       }
-    }
-  }
-  for (int bb = nb + tid; bb < NB; bb += nthreads) beamA[bb] = 0.f;
-  if (h == 0) {  // the rest of each row: own slot, then -1; rows of beams >= n are all -1
-    for (int idx = tid; idx < nb * (L - nch); idx += nthreads) {
-      const int bb = idx / (L - nch), m = nch + idx - bb * (L - nch);
-      a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = m == nch ? nch * a.B_max + b0 + bb : -1;
-    }
-    if (tile == ntile - 1) {
-      for (int idx = tid; idx < (a.B_max - n) * L; idx += nthreads)
-        a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
-    }
-  }
-  __syncthreads();
-
-  // ---- after the chain tables: every remaining global load is a gather whose address comes from LDS.  The
-  // gathers run as software pipelines of unconditional loads (indices past the end are clamped to a valid
-  // record and their values dropped), so that the compiler's in-order vmcnt waits cover exactly the load
-  // being consumed and never the ones issued after it.
-  const int g16 = tid >> 4, j16 = tid & 15;
-  const int ngroups = nthreads >> 4;
-  auto rest = [&](auto rm_c) {
-    constexpr int RM = decltype(rm_c)::value;  // chain records per tile in flight in the u ring (0: no chain)
-    constexpr int NU = RM > 0 ? RM * kTiles : 1;
-    int bcs[kTiles];  // this lane's beam in each 16-beam tile, clamped to the tile's last beam
-#pragma unroll
-    for (int mt = 0; mt < kTiles; ++mt) bcs[mt] = min(mt * 16 + col, nb - 1);
-    auto u_load = [&](int mt, int m) -> f32x4_t {
-      const unsigned uo = u_index((unsigned)slot_tab[bcs[mt] * LS + m], (unsigned)dv0, (unsigned)d_v);
-      return *reinterpret_cast<const f32x4_t*>(u_rd + uo);
+      for (int idx = tid + kPV * nthreads; idx < NB * vc; idx += nthreads) {
+        const int bb = idx / vc;
+        *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = v_piece(idx);
+      }
     };
-    // u ring, records-major: U[r * kTiles + mt] holds record m0 + r of tile mt.  Its first RM records go out
-    // now and land during phase 1.
-    f32x4_t U[NU];
-    if constexpr (RM > 0) {
-#pragma unroll
-      for (int r = 0; r < RM; ++r)
-#pragma unroll
-        for (int mt = 0; mt < kTiles; ++mt) U[r * kTiles + mt] = u_load(mt, min(r, nch - 1));
+    const int gq = lane >> 4, col = lane & 15;
+    const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
+    constexpr int kTiles = NB / 16;
+    if constexpr (!PERSIST) load_sf(wave, lane);
+    __builtin_amdgcn_sched_barrier(0);  // every streaming request is out before the parents are consumed
+    if (tid >= nb) {
+      pP = 0;
+      pAl = 0.f;
+      pBe = 0.f;
     }
+    if (tid < NB) {
+      // sticky flag; decode as a child of beam 0 so that accesses stay in bounds
+      if (tid < nb && (pP < 0 || pP >= a.b_prev)) {
+        *a.flag = a.epoch;
+        pP = 0;
+      }
+      beamPar[tid] = pP;
+      beamAl[tid] = pAl;
+      beamBe[tid] = pBe;
+    }
+    __syncthreads();
 
-    // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q into the coefficient table.  Group g
-    // takes items g, g + ngroups, ...; a ring of kD1 chain keys per lane. ----
-    if constexpr (RM > 0) {
-      const int items = nb * nch;
-      const int kmax = (items + ngroups - 1) / ngroups;
-      u32x4_t K[kD1];
-      int IY[kD1];
-      auto k_load = [&](int kk, int d) {
-        const int2 e = item_tab[min(kk * ngroups + g16, items - 1)];
-        IY[d] = e.y;
-        K[d] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)e.x * kDK + j16 * 8));
-      };
-      auto k_use = [&](int kk, int d) {
-        if (kk * ngroups + g16 < items) {  // uniform over the 16 lanes of the group
-          const int pos = IY[d] & 0xFFFF, bb = IY[d] >> 16;
-          const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
-          const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
-          const float dk = row16_sum(dot8_bf16(K[d], kx));
-          const float dq = row16_sum(dot8_bf16(K[d], qx));
-          if (j16 == 0) {
-            const float c = c_tab[pos];
-            coef[pos] = (f32x2_t){c * dk, c * dq};
+    // ---- phase 0 (cont.): the parents' chain rows and decay rows in one round trip; this step's rows ----
+    const int drow = L + 1;    // decay row: c_0 .. c_{L-1}, then A
+    const int nper = nch + 1;  // per beam: nch chain entries, then the parent's total decay A
+    int raw[4];
+    float dec[4];
+    auto chain_load = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * nthreads + tid;
+        raw[u] = 0;
+        dec[u] = 1.f;
+        if (idx < nb * nper) {
+          const int bb = idx / nper, m = idx - bb * nper;
+          if (m < nch) {
+            raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
+            dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
+          } else if (nch > 0) {
+            dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L];
           }
         }
-      };
+      }
+    };
+    chain_load(0);
+    store_x();
+    for (int base = 0; base < nb * nper; base += 4 * nthreads) {
+      if (base > 0) chain_load(base);
 #pragma unroll
-      for (int d = 0; d < kD1; ++d) k_load(d, d);
-      int k0 = 0;
-      for (; k0 + kD1 < kmax; k0 += kD1) {
-#pragma unroll
-        for (int d = 0; d < kD1; ++d) {
-          k_use(k0 + d, d);
-          k_load(k0 + kD1 + d, d);
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * nthreads + tid;
+        if (idx < nb * nper) {
+          const int bb = idx / nper, m = idx - bb * nper;
+          float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
+          if (m < nch) {
+            const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
+            slot_tab[bb * LS + m] = sl;
+            c_tab[bb * LS + m] = dec[u];
+            item_tab[bb * nch + m] = make_int2(sl, (bb << 16) | (bb * LS + m));
+            dout[m] = dec[u] * beamAl[bb];
+            if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
+          } else {
+            dout[nch] = 1.f;
+            dout[L] = dec[u] * beamAl[bb];
+            beamA[bb] = dec[u];
+          }
         }
       }
-#pragma unroll
-      for (int d = 0; d < kD1; ++d) k_use(k0 + d, d);
     }
-    // k . q of every beam; append the record key and alpha
-    for (int bb = g16; bb < nb; bb += ngroups) {
-      const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
-      const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
-      const float kq = row16_sum(dot8_bf16(kx, qx));
-      const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-      *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j16 * 8)) = kx;
-      if (j16 == 0) {
-        beamKq[bb] = kq;
-        al_wr[own] = beamAl[bb];
+    for (int bb = nb + tid; bb < NB; bb += nthreads) beamA[bb] = 0.f;
+    if (h == 0) {  // the rest of each row: own slot, then -1; rows of beams >= n are all -1
+      for (int idx = tid; idx < nb * (L - nch); idx += nthreads) {
+        const int bb = idx / (L - nch), m = nch + idx - bb * (L - nch);
+        a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = m == nch ? nch * a.B_max + b0 + bb : -1;
+      }
+      if (tile == ntile - 1) {
+        for (int idx = tid; idx < (a.B_max - n) * L; idx += nthreads)
+          a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
       }
     }
     __syncthreads();
 
-    // ---- phase 2: the replay over the u ring (sums per tile in P, Q), then per tile the MFMA contraction,
-    // u and o ----
-    floatx4_t P[kTiles], Q[kTiles];
+    // ---- after the chain tables: every remaining global load is a gather whose address comes from LDS.  The
+    // gathers run as software pipelines of unconditional loads (indices past the end are clamped to a valid
+    // record and their values dropped), so that the compiler's in-order vmcnt waits cover exactly the load
+    // being consumed and never the ones issued after it.
+    const int g16 = tid >> 4, j16 = tid & 15;
+    const int ngroups = nthreads >> 4;
+    auto rest = [&](auto rm_c) {
+      constexpr int RM = decltype(rm_c)::value;  // chain records per tile in flight in the u ring (0: no chain)
+      constexpr int NU = RM > 0 ? RM * kTiles : 1;
+      int bcs[kTiles];  // this lane's beam in each 16-beam tile, clamped to the tile's last beam
 #pragma unroll
-    for (int mt = 0; mt < kTiles; ++mt) {
-      P[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      Q[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-    }
-    if constexpr (RM > 0) {
-      auto acc = [&](int mt, int m, int i) {
-        if (mt * 16 < nb) {
-          const f32x2_t c = coef[bcs[mt] * LS + m];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            P[mt][e] += c.x * U[i][e];
-            Q[mt][e] += c.y * U[i][e];
-          }
-        }
+      for (int mt = 0; mt < kTiles; ++mt) bcs[mt] = min(mt * 16 + col, nb - 1);
+      auto u_load = [&](int mt, int m) -> f32x4_t {
+        const unsigned uo = u_index((unsigned)slot_tab[bcs[mt] * LS + m], (unsigned)dv0, (unsigned)d_v);
+        return *reinterpret_cast<const f32x4_t*>(u_rd + uo);
       };
-      int m0 = 0;
-      for (; m0 + RM < nch; m0 += RM) {
+      // u ring, records-major: U[r * kTiles + mt] holds record m0 + r of tile mt.  Its first RM records go out
+      // now and land during phase 1.
+      f32x4_t U[NU];
+      if constexpr (RM > 0) {
 #pragma unroll
         for (int r = 0; r < RM; ++r)
 #pragma unroll
-          for (int mt = 0; mt < kTiles; ++mt) {
-            acc(mt, m0 + r, r * kTiles + mt);
-            U[r * kTiles + mt] = u_load(mt, min(m0 + RM + r, nch - 1));
+          for (int mt = 0; mt < kTiles; ++mt) U[r * kTiles + mt] = u_load(mt, min(r, nch - 1));
+      }
+
+      // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q into the coefficient table.  Group g
+      // takes items g, g + ngroups, ...; a ring of kD1 chain keys per lane. ----
+      if constexpr (RM > 0) {
+        const int items = nb * nch;
+        const int kmax = (items + ngroups - 1) / ngroups;
+        u32x4_t K[kD1];
+        int IY[kD1];
+        auto k_load = [&](int kk, int d) {
+          const int2 e = item_tab[min(kk * ngroups + g16, items - 1)];
+          IY[d] = e.y;
+          K[d] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)e.x * kDK + j16 * 8));
+        };
+        auto k_use = [&](int kk, int d) {
+          if (kk * ngroups + g16 < items) {  // uniform over the 16 lanes of the group
+            const int pos = IY[d] & 0xFFFF, bb = IY[d] >> 16;
+            const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
+            const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
+            const float dk = row16_sum(dot8_bf16(K[d], kx));
+            const float dq = row16_sum(dot8_bf16(K[d], qx));
+            if (j16 == 0) {
+              const float c = c_tab[pos];
+              coef[pos] = (f32x2_t){c * dk, c * dq};
+            }
+          }
+        };
+#pragma unroll
+        for (int d = 0; d < kD1; ++d) k_load(d, d);
+        int k0 = 0;
+        for (; k0 + kD1 < kmax; k0 += kD1) {
+#pragma unroll
+          for (int d = 0; d < kD1; ++d) {
+            k_use(k0 + d, d);
+            k_load(k0 + kD1 + d, d);
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < kD1; ++d) k_use(k0 + d, d);
+      }
+      // k . q of every beam; append the record key and alpha
+      for (int bb = g16; bb < nb; bb += ngroups) {
+        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
+        const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
+        const float kq = row16_sum(dot8_bf16(kx, qx));
+        const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
+        *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j16 * 8)) = kx;
+        if (j16 == 0) {
+          beamKq[bb] = kq;
+          al_wr[own] = beamAl[bb];
+        }
+      }
+      __syncthreads();
+
+      // ---- phase 2: the replay over the u ring (sums per tile in P, Q), then per tile the MFMA contraction,
+      // u and o ----
+      floatx4_t P[kTiles], Q[kTiles];
+#pragma unroll
+      for (int mt = 0; mt < kTiles; ++mt) {
+        P[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+        Q[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      }
+      if constexpr (RM > 0) {
+        auto acc = [&](int mt, int m, int i) {
+          if (mt * 16 < nb) {
+            const f32x2_t c = coef[bcs[mt] * LS + m];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              P[mt][e] += c.x * U[i][e];
+              Q[mt][e] += c.y * U[i][e];
+            }
+          }
+        };
+        int m0 = 0;
+        for (; m0 + RM < nch; m0 += RM) {
+#pragma unroll
+          for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int mt = 0; mt < kTiles; ++mt) {
+              acc(mt, m0 + r, r * kTiles + mt);
+              U[r * kTiles + mt] = u_load(mt, min(m0 + RM + r, nch - 1));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+          if (m0 + r < nch) {
+#pragma unroll
+            for (int mt = 0; mt < kTiles; ++mt) acc(mt, m0 + r, r * kTiles + mt);
           }
       }
 #pragma unroll
-      for (int r = 0; r < RM; ++r)
-        if (m0 + r < nch) {
+      for (int mt = 0; mt < kTiles; ++mt) {
+        if (mt * 16 >= nb) break;
+        const int bb = mt * 16 + col;
+        floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+        // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
 #pragma unroll
-          for (int mt = 0; mt < kTiles; ++mt) acc(mt, m0 + r, r * kTiles + mt);
+        for (int ks = 0; ks < kKS; ++ks) {
+          const bf16x8_t bk = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
+          const bf16x8_t bq = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
+            pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
+          }
         }
-    }
+        if (bb < nb) {
+          const float A = beamA[bb], al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
+          const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
+          const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bb * lay.vrow + dv0 * 2);
+          const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
+          const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
+                               bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
+          f32x4_t u4, o4;
 #pragma unroll
-    for (int mt = 0; mt < kTiles; ++mt) {
-      if (mt * 16 >= nb) break;
-      const int bb = mt * 16 + col;
-      floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8_t bk = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
-        const bf16x8_t bq = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
-          pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const float uu = be * (v4[e] - al * (A * pk[e] + P[mt][e]));
+            u4[e] = uu;
+            o4[e] = al * (A * pq[e] + Q[mt][e]) + kq * uu;
+          }
+          *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
+          *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
         }
       }
-      if (bb < nb) {
-        const float A = beamA[bb], al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
-        const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-        const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bb * lay.vrow + dv0 * 2);
-        const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
-        const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
-                             bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
-        f32x4_t u4, o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float uu = be * (v4[e] - al * (A * pk[e] + P[mt][e]));
-          u4[e] = uu;
-          o4[e] = al * (A * pq[e] + Q[mt][e]) + kq * uu;
-        }
-        *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
-        *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
-      }
-    }
+    };
+    if (nch == 0)
+      rest(IntC<0>{});
+    else if (nch == 1)
+      rest(IntC<1>{});
+    else
+      rest(IntC<(NB >= 128 ? 1 : kRM)>{});  // 8 tiles per lane: one record per tile in flight
   };
-  if (nch == 0)
-    rest(IntC<0>{});
-  else if (nch == 1)
-    rest(IntC<1>{});
-  else
-    rest(IntC<(NB >= 128 ? 1 : kRM)>{});  // 8 tiles per lane: one record per tile in flight
+
+  if constexpr (PERSIST) {
+    load_sf((int)threadIdx.x >> 6, (int)threadIdx.x & 63);
+    const int tile_end = min(ntile, (split + 1) * tps);
+    for (int tile = split * tps; tile < tile_end; ++tile) {
+      // the thread index is laundered per tile, so that the compiler derives the per-lane addresses next to
+      // their use instead of keeping them live (and spilled) across the loop
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      do_tile(tile, tid);
+      if (tile + 1 < tile_end) __syncthreads();  // the next tile overwrites the LDS tables
+    }
+  } else {
+    do_tile(split, (int)threadIdx.x);
+  }
 }
 
 bool fused_supported(int d_k, int d_v, int L_max) {
@@ -461,19 +486,34 @@ int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
   return 16;
 }
 
+namespace {
+using FusedKernel = void (*)(StepArgs, int, int);
+hipError_t launch_fused_as(FusedKernel k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const StepArgs& a,
+                           int ntile, int tps) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, grid, block, lds, s, a, ntile, tps);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s) {
   const int ntile = (a.n + tile - 1) / tile;
-  dim3 grid((unsigned)((size_t)a.R * a.H * ntile)), block(4 * a.d_v);
+  // A workgroup has d_v / 16 waves of up to 128 VGPRs: the register file admits 16 / (d_v / 16) per CU.  When
+  // it admits one, each workgroup runs kPersistTiles consecutive tiles of its (request, head): no CU then idles
+  // between one workgroup's last store and the next one's launch, and S_ctx is read once per run.
+  const bool persist = 16 / (a.d_v / 16) < 2;
+  const int tps = persist ? std::min(ntile, kPersistTiles) : 1;
+  const int nsplit = (ntile + tps - 1) / tps;
+  dim3 grid((unsigned)((size_t)a.R * a.H * nsplit)), block(4 * a.d_v);
   const size_t lds = fused_lds_bytes(tile, a.L_max, a.d_v);
-#define ONELA_FUSED_CASE(NB)                                                                                   \
-  case NB:                                                                                                     \
-    if (lds > 64 * 1024) {                                                                                     \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_fused_kernel<NB>),                \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
-      if (e != hipSuccess) return e;                                                                           \
-    }                                                                                                          \
-    hipLaunchKernelGGL(step_fused_kernel<NB>, grid, block, lds, s, a, ntile);                                  \
-    break;
+#define ONELA_FUSED_CASE(NB)                                                                     \
+  case NB:                                                                                       \
+    return persist ? launch_fused_as(&step_fused_kernel<NB, true>, grid, block, lds, s, a, ntile, tps) \
+                   : launch_fused_as(&step_fused_kernel<NB, false>, grid, block, lds, s, a, ntile, tps);
   switch (tile) {
     ONELA_FUSED_CASE(16)
     ONELA_FUSED_CASE(32)
@@ -483,7 +523,6 @@ hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s) {
       return hipErrorInvalidValue;
   }
 #undef ONELA_FUSED_CASE
-  return hipGetLastError();
 }
 
 }  // namespace onela
