@@ -13,7 +13,8 @@
 //            beam's chain is its parent's chain from the previous table plus its own slot; the head-0
 //            workgroups write the new table.  The decays along a chain (A = prod alpha, c_j = prod of the
 //            alphas after record j) are kept per (request, head, beam) next to the index: a beam reads its
-//            parent's row (chain entries and A in one round trip), and writes its own (c_j alpha_b for the
+//            parent's row (chain entries and A in one round trip, issued by the thread that holds the parent
+//            as soon as it arrives, with no barrier before it), and writes its own (c_j alpha_b for the
 //            parent's records, 1 for its own record, A alpha_b) for the next step, so no record alpha is
 //            gathered.
 //   Phase 1  the u of the chain records (this lane's 4-row piece of each of its 4 beams) starts streaming
@@ -46,6 +47,7 @@ constexpr int kKS = kDK / 32;        // MFMA k-steps
 constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
 constexpr int kD1 = 4;               // chain keys in flight per lane (phase 1)
 constexpr int kRM = 2;               // chain records per tile in flight per lane (phase 2)
+constexpr int kChainChunk = 8;      // chain entries per round trip of the parent-row reads
 constexpr int kPersistTiles = 4;     // tiles per workgroup when one workgroup fills a CU
 
 template <int V>
@@ -56,7 +58,7 @@ constexpr int kPX = 4;               // 16-byte pieces of the k and q rows per t
 constexpr int kPV = 2;               // 16-byte pieces of the v rows per thread held in registers
 
 struct FusedLds {
-  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, beamPar, vs, vrow, total;
+  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, vs, vrow, total;
 };
 
 // Per-beam tables use an odd row stride so that 16 beams read by one wave fall in distinct LDS banks.
@@ -75,7 +77,6 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L, int d_v) {
   l.beamAl = off;  off += NB * 4;
   l.beamBe = off;  off += NB * 4;
   l.beamKq = off;  off += NB * 4;
-  l.beamPar = off; off += NB * 4;
   l.vrow = d_v * 2 + 16;
   l.vs = off;      off += NB * l.vrow;     // v rows (bf16, padded like the k and q rows)
   l.total = off;
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile,
     float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
     float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
     float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
-    int* beamPar = reinterpret_cast<int*>(lds + lay.beamPar);
     const int lane = tid & 63, wave = tid >> 6;
     const int b0 = tile * NB;
     const int nb = min(NB, n - b0);
@@ -220,76 +220,68 @@ __global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile,
       pAl = 0.f;
       pBe = 0.f;
     }
+    // ---- phase 0 (cont.): thread tid < NB holds beam tid's parent and reads the parent's chain row and decay
+    // row itself, as soon as the parent has arrived (no barrier before this round trip); this step's rows.
+    // Loads are unconditional (entries past the chain are clamped to its last one and dropped). ----
+    const int drow = L + 1;  // decay row: c_0 .. c_{L-1}, then A
     if (tid < NB) {
       // sticky flag; decode as a child of beam 0 so that accesses stay in bounds
       if (tid < nb && (pP < 0 || pP >= a.b_prev)) {
         *a.flag = a.epoch;
         pP = 0;
       }
-      beamPar[tid] = pP;
       beamAl[tid] = pAl;
       beamBe[tid] = pBe;
-    }
-    __syncthreads();
-
-    // ---- phase 0 (cont.): the parents' chain rows and decay rows in one round trip; this step's rows ----
-    const int drow = L + 1;    // decay row: c_0 .. c_{L-1}, then A
-    const int nper = nch + 1;  // per beam: nch chain entries, then the parent's total decay A
-    int raw[4];
-    float dec[4];
-    auto chain_load = [&](int base) {
+      const bool live = tid < nb;
+      float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + tid) * drow;
+      int32_t* cout = a.chain_out + ((size_t)r * a.B_max + b0 + tid) * L;
+      if (nch > 0) {
+        const int32_t* crow = a.chain_prev + ((size_t)r * a.B_max + pP) * L;
+        const float* drw = a.decay_prev + ((size_t)rh * a.B_max + pP) * drow;
+        const float Ap = drw[L];
+        for (int m0 = 0; m0 < nch; m0 += kChainChunk) {
+          int raw[kChainChunk];
+          float dec[kChainChunk];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * nthreads + tid;
-        raw[u] = 0;
-        dec[u] = 1.f;
-        if (idx < nb * nper) {
-          const int bb = idx / nper, m = idx - bb * nper;
-          if (m < nch) {
-            raw[u] = a.chain_prev[((size_t)r * a.B_max + beamPar[bb]) * L + m];
-            dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + m];
-          } else if (nch > 0) {
-            dec[u] = a.decay_prev[((size_t)rh * a.B_max + beamPar[bb]) * drow + L];
+          for (int u = 0; u < kChainChunk; ++u) {
+            const int m = min(m0 + u, nch - 1);
+            raw[u] = crow[m];
+            dec[u] = drw[m];
+          }
+#pragma unroll
+          for (int u = 0; u < kChainChunk; ++u) {
+            const int m = m0 + u;
+            if (live && m < nch) {
+              const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
+              slot_tab[tid * LS + m] = sl;
+              c_tab[tid * LS + m] = dec[u];
+              item_tab[tid * nch + m] = make_int2(sl, (tid << 16) | (tid * LS + m));
+              dout[m] = dec[u] * pAl;
+              if (h == 0) cout[m] = raw[u];
+            }
           }
         }
+        if (live) {
+          dout[nch] = 1.f;
+          dout[L] = Ap * pAl;
+        }
+        beamA[tid] = live ? Ap : 0.f;
+      } else {
+        if (live) {
+          dout[0] = 1.f;
+          dout[L] = pAl;
+        }
+        beamA[tid] = live ? 1.f : 0.f;
       }
-    };
-    chain_load(0);
+      if (h == 0 && live) {  // the rest of the row: own slot, then -1
+        for (int m = nch; m < L; ++m) cout[m] = m == nch ? nch * a.B_max + b0 + tid : -1;
+      }
+    }
+    if (h == 0 && tile == ntile - 1) {  // rows of beams >= n are all -1
+      for (int idx = tid; idx < (a.B_max - n) * L; idx += nthreads)
+        a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
+    }
     store_x();
-    for (int base = 0; base < nb * nper; base += 4 * nthreads) {
-      if (base > 0) chain_load(base);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * nthreads + tid;
-        if (idx < nb * nper) {
-          const int bb = idx / nper, m = idx - bb * nper;
-          float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + bb) * drow;
-          if (m < nch) {
-            const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
-            slot_tab[bb * LS + m] = sl;
-            c_tab[bb * LS + m] = dec[u];
-            item_tab[bb * nch + m] = make_int2(sl, (bb << 16) | (bb * LS + m));
-            dout[m] = dec[u] * beamAl[bb];
-            if (h == 0) a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = raw[u];
-          } else {
-            dout[nch] = 1.f;
-            dout[L] = dec[u] * beamAl[bb];
-            beamA[bb] = dec[u];
-          }
-        }
-      }
-    }
-    for (int bb = nb + tid; bb < NB; bb += nthreads) beamA[bb] = 0.f;
-    if (h == 0) {  // the rest of each row: own slot, then -1; rows of beams >= n are all -1
-      for (int idx = tid; idx < nb * (L - nch); idx += nthreads) {
-        const int bb = idx / (L - nch), m = nch + idx - bb * (L - nch);
-        a.chain_out[((size_t)r * a.B_max + b0 + bb) * L + m] = m == nch ? nch * a.B_max + b0 + bb : -1;
-      }
-      if (tile == ntile - 1) {
-        for (int idx = tid; idx < (a.B_max - n) * L; idx += nthreads)
-          a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
-      }
-    }
     __syncthreads();
 
     // ---- after the chain tables: every remaining global load is a gather whose address comes from LDS.  The
