@@ -131,12 +131,12 @@ hipError_t launch_split_frag(const float* ST, uint16_t* frag, int RH, int d_v, i
 // state), the gated delta rule of Gated DeltaNet (paper index page, "Builds on"):
 //   p = S k,  u = beta (v - alpha p),  S <- alpha S + u k^T.
 // Row i of S evolves on its own: it needs v_i and the token's shared k, alpha and beta, nothing from the
-// other rows.  So the recurrence is split over rows, 8 lanes per row: lane j of a row holds the columns of
-// float4 groups j, j + 8, j + 16, ... of d_k (padded with zero columns to a multiple of 32) in registers,
-// and p is summed over the row's 8 lanes with DPP, with no barrier per token.  A workgroup of 1024 threads
-// takes 128 rows of one (request, head).  Tokens come in blocks of kPfT: k, the workgroup's v entries,
-// alpha and beta of a block are staged in LDS (two buffers, one barrier per block), fetched from HBM into
-// registers one block ahead.
+// other rows.  So the recurrence is split over rows, LANES lanes per row (4 up to d_k = 128, else 8): lane j
+// of a row holds the columns of float4 groups j, j + LANES, j + 2 LANES, ... of d_k (padded with zero columns
+// to a multiple of 32) in registers, and p is summed over the row's lanes with DPP, with no barrier per
+// token.  A workgroup of 128 LANES threads takes 128 rows of one (request, head).  Tokens come in blocks of
+// kPfT: k, the workgroup's v entries, alpha and beta of a block are staged in LDS (two buffers, one barrier
+// per block), fetched from HBM into registers one block ahead.
 // The decay is carried as a scale, S = g Ŝ with g the running product of alpha: a token then costs one
 // FMA per element for the update, Ŝ += (u / g) k^T.  When g falls below 2^-20 (also when alpha = 0) it
 // is folded into Ŝ and reset to 1.
@@ -144,21 +144,25 @@ hipError_t launch_split_frag(const float* ST, uint16_t* frag, int RH, int d_v, i
 namespace {
 constexpr int kPfT = 16;                 // tokens per staged block
 constexpr int kPfRows = 128;             // rows of S per workgroup
-constexpr int kPfThreads = 8 * kPfRows;  // 8 lanes per row
 constexpr float kPfRenorm = 0x1p-20f;
 }  // namespace
+
+// Lanes per row of S for d_k padded to 32 * per4 columns: 4 up to d_k = 128 (32 state columns per lane; fewer
+// lanes per row mean fewer DPP steps and LDS reads per FMA), 8 above (the register state would not fit).
+constexpr int prefill_lanes(int per4) { return per4 <= 4 ? 4 : 8; }
 
 // LDS per buffer: k [kPfT][d_kp], v [kPfT][kPfRows], alpha and beta [kPfT]
 inline size_t prefill_lds_bytes(int d_kp) { return 2 * (size_t)(kPfT * (d_kp + kPfRows + 2)) * sizeof(float); }
 
-template <int PER4>  // d_k padded to 32 * PER4 columns
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __restrict__ kin,
+template <int PER4, int LANES>  // d_k padded to 32 * PER4 columns; LANES lanes per row of S
+__global__ __launch_bounds__(LANES * kPfRows) void prefill_kernel(const float* __restrict__ kin,
                                                              const float* __restrict__ vin,
                                                              const float* __restrict__ ain,
                                                              const float* __restrict__ bin, int H, int N, int d_k,
                                                              int d_v, int nrb, float* __restrict__ sctx_t,
                                                              float* __restrict__ sctx_out) {
   extern __shared__ __align__(16) float pf_lds[];
+  constexpr int kPfLanes = LANES, kPfThreads = LANES * kPfRows;
   constexpr int d_kp = 32 * PER4;
   constexpr int buf_floats = kPfT * (d_kp + kPfRows + 2);
   constexpr int kLd = (kPfT * d_kp + kPfThreads - 1) / kPfThreads;  // staged k elements per thread
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __rest
   const int rh = blockIdx.x / nrb, rb = blockIdx.x - rh * nrb;
   const int r = rh / H, h = rh - r * H;
   const int tid = threadIdx.x;
-  const int row = tid >> 3, j = tid & 7;
+  const int row = tid / kPfLanes, j = tid % kPfLanes;
   const int i = rb * kPfRows + row;  // this lane's row of S (beyond d_v: computed on zeros, not stored)
   const size_t tok0 = (size_t)r * N * H + h;  // token n of this (request, head): index tok0 + n * H
 
@@ -200,9 +204,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __rest
     if (tid < 2 * kPfT) base[kPfT * (d_kp + kPfRows) + tid] = abr;  // (alpha, beta) pairs per token
   };
 
-  float S[4 * PER4];
+  constexpr int kG = 8 * PER4 / kPfLanes;  // float4 column groups per lane
+  float S[4 * kG];
 #pragma unroll
-  for (int e = 0; e < 4 * PER4; ++e) S[e] = 0.f;
+  for (int e = 0; e < 4 * kG; ++e) S[e] = 0.f;
   float g = 1.f;  // S = g * (the registers)
   const int nblk = (N + kPfT - 1) / kPfT;
   if (nblk > 0) {
@@ -218,32 +223,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __rest
     const float* ab = vb + kPfT * kPfRows;
     const int ntok = min(kPfT, N - blk * kPfT);
     for (int tt = 0; tt < ntok; ++tt) {
-      f32x4_t kk[PER4];
+      f32x4_t kk[kG];
 #pragma unroll
-      for (int m = 0; m < PER4; ++m) kk[m] = *reinterpret_cast<const f32x4_t*>(kb + tt * d_kp + 4 * (j + 8 * m));
+      for (int m = 0; m < kG; ++m) kk[m] = *reinterpret_cast<const f32x4_t*>(kb + tt * d_kp + 4 * (j + kPfLanes * m));
       const float vi = vb[tt * kPfRows + row];
       const f32x2_t a_b = *reinterpret_cast<const f32x2_t*>(ab + 2 * tt);
       f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < PER4; ++m)
+      for (int m = 0; m < kG; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += S[4 * m + e] * kk[m][e];
       float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      // sum over the row's 8 lanes: swap neighbours, swap pairs, mirror within the half row
+      // sum over the row's lanes: swap neighbours, swap pairs (then, for 8 lanes, mirror within the half row)
       dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0xB1, 0xF, 0xF, true));
       dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x4E, 0xF, 0xF, true));
-      dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x141, 0xF, 0xF, true));
+      if constexpr (kPfLanes == 8)
+        dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x141, 0xF, 0xF, true));
       const float alpha = a_b.x, beta = a_b.y;
       const float u = beta * (vi - alpha * (g * dot));
       float gn = alpha * g;
       if (gn < kPfRenorm) {  // the same decision in every lane (alpha and g are shared)
 #pragma unroll
-        for (int e = 0; e < 4 * PER4; ++e) S[e] *= gn;
+        for (int e = 0; e < 4 * kG; ++e) S[e] *= gn;
         gn = 1.f;
       }
       const float c = u * __builtin_amdgcn_rcpf(gn);
 #pragma unroll
-      for (int m = 0; m < PER4; ++m)
+      for (int m = 0; m < kG; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[4 * m + e] += c * kk[m][e];
       g = gn;
@@ -255,10 +261,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(const float* __rest
     float* dst = sctx_t + (size_t)rh * d_k * d_v;
     float* so = sctx_out ? sctx_out + ((size_t)rh * d_v + i) * d_k : nullptr;
 #pragma unroll
-    for (int m = 0; m < PER4; ++m)
+    for (int m = 0; m < kG; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int col = 4 * (j + 8 * m) + e;
+        const int col = 4 * (j + kPfLanes * m) + e;
         if (col < d_k) {
           const float x = g * S[4 * m + e];
           dst[(size_t)col * d_v + i] = x;
@@ -275,16 +281,16 @@ hipError_t launch_prefill(const float* k, const float* v, const float* alpha, co
   const int per4 = (d_k + 31) / 32;
   const int nrb = (d_v + kPfRows - 1) / kPfRows;
   const size_t lds = prefill_lds_bytes(32 * per4);
-  dim3 grid((unsigned)((size_t)R * H * nrb)), block(kPfThreads);
+  dim3 grid((unsigned)((size_t)R * H * nrb)), block(prefill_lanes(per4) * kPfRows);
 #define ONELA_PREFILL_CASE(P)                                                                                  \
   case P:                                                                                                      \
     if (lds > 64 * 1024) {                                                                                     \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<P>),                   \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<P, prefill_lanes(P)>), \
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
       if (e != hipSuccess) return e;                                                                           \
     }                                                                                                          \
-    hipLaunchKernelGGL(prefill_kernel<P>, grid, block, lds, s, k, v, alpha, beta, H, N, d_k, d_v, nrb, sctx_t,  \
-                       sctx_out);                                                                              \
+    hipLaunchKernelGGL((prefill_kernel<P, prefill_lanes(P)>), grid, block, lds, s, k, v, alpha, beta, H, N, d_k, \
+                       d_v, nrb, sctx_t, sctx_out);                                                            \
     break;
   switch (per4) {
     ONELA_PREFILL_CASE(1)
