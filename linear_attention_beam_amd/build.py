@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "lib", "libonela.so")
 SOURCES = ["onela_host.cpp", "context.hip", "step_generic.hip", "step_fused.hip", "fullstate.hip",
-           "beam_select.hip", "materialize.hip"]
+           "beam_select.hip", "materialize.hip", "prefill_mfma.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.

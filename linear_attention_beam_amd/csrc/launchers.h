@@ -41,6 +41,10 @@ hipError_t launch_split_frag(const float* ST, uint16_t* frag, int RH, int d_v, i
 hipError_t launch_prefill(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
                           int N, int d_k, int d_v, float* sctx_t, float* sctx_out, hipStream_t s);
 bool prefill_supported(int d_k, int d_v);
+// chunked prefill on MFMA (d_k = 128, d_v in {16, 32, 64, 128, 256}); same outputs as launch_prefill
+bool prefill_mfma_supported(int d_k, int d_v);
+hipError_t launch_prefill_mfma(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
+                               int N, int d_v, float* sctx_t, float* sctx_out, hipStream_t s);
 
 hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Materializing replay (comparison path): dense parent state rebuilt per pair and step.

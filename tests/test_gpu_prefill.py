@@ -1,6 +1,8 @@
-"""GPU prefill (onela_prefill) against the float64 oracle prefill: head sizes that are not multiples of the
-kernel's 32-column groups or 128-row workgroups, token counts that leave a ragged last block, no tokens,
-and decays small enough (or zero) to exercise the folding of the decay scale into the state."""
+"""GPU prefill (onela_prefill) against the float64 oracle prefill.  d_k = 128 with d_v in {16, 32, 64, 128, 256}
+runs the chunked MFMA kernel (32-token chunks: token counts that leave a ragged last chunk, or fewer tokens than
+one chunk); other head sizes run the row-parallel fp32 kernel (sizes that are not multiples of its 32-column
+groups or 128-row workgroups).  Also: no tokens, and decays small enough (or zero) to exercise the folding of
+the decay scale into the state (fp32 kernel) and the running decay products (MFMA kernel)."""
 
 import numpy as np
 import pytest
@@ -41,7 +43,7 @@ def check(cfg, pf):
 
 @pytest.mark.parametrize("d_k,d_v,N", [
     (128, 128, 100), (16, 16, 17), (64, 32, 1), (96, 200, 33), (256, 256, 40), (40, 7, 16), (1, 1, 5),
-    (200, 130, 31), (128, 256, 48),
+    (200, 130, 31), (128, 256, 48), (128, 64, 70), (128, 32, 33), (128, 16, 65), (128, 128, 1), (128, 96, 40),
 ])
 def test_prefill_shapes(d_k, d_v, N):
     cfg = inputs.config(2, R=2, H=3, d_k=d_k, d_v=d_v, prefill_steps=N)
