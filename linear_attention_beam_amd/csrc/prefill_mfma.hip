@@ -20,12 +20,13 @@
 // 8 g + j of lane l stands for index 4 g + j (j < 4) or 16 + 4 g + j - 4 (j >= 4) of the 32: that is exactly
 // which of its own accumulator values a lane holds, so S^T, X and U feed the next product without moving
 // between lanes; the matching operands are read from LDS in the same order.
-// T depends on the chunk's k, alpha and beta only, so it is formed ahead, 8 chunks at a time in parallel:
-//   phase A  wave w forms T of chunk 8 q + w (G = K K^T on MFMA with k read from HBM, M, the two 16 x 16
+// T depends on the chunk's k, alpha and beta only, so it is formed ahead for a group of chunks in parallel
+// (as many as the workgroup has waves, at most 8):
+//   phase A  wave w forms T of chunk w of the group (G = K K^T on MFMA with k read from HBM, M, the two 16 x 16
 //            diagonal blocks of T by forward substitution, the off-diagonal block as -D M21 A) in a 32 x 32
 //            scratch of its own, and leaves T's MFMA operands (bf16 high/low, in lane order), gamma, rc and beta
 //            in a group buffer;
-//   phase B  the 8 chunks in turn: v, the k rows (bf16 high/low) and float32 k go to LDS (one chunk ahead
+//   phase B  the group's chunks in turn: v, the k rows (bf16 high/low) and float32 k go to LDS (one chunk ahead
 //            in registers), then k scaled by rc is transposed in LDS, then every wave runs its three products.
 // Tokens past the end pad with k = 0, v = 0, alpha = 1, beta = 0: a token that leaves the state unchanged.
 #include "device_common.h"
@@ -41,7 +42,8 @@ constexpr int kKRow = 136;  // bf16 per row of the K rows (128 + 8 padding)
 constexpr int kFRow = 132;  // floats per row of the float32 K rows
 constexpr int kTRow = 36;   // bf16 per row of the transposed K rows (32 + 4 padding)
 constexpr int kGRow = 36;   // floats per row of a wave's 32 x 32 scratch
-constexpr int kTOp = 2 * 64 * 32;  // bytes of T's MFMA operands per chunk: 2 row blocks x 64 lanes x (16 B high, 16 B low)
+// bytes of T's MFMA operands per chunk: 2 row blocks x 64 lanes x (16 bytes high, 16 bytes low)
+constexpr int kTOp = 2 * 64 * 32;
 
 struct PmLds {
   int grp_t, grp_s, scr, kh, kl, kf, kth, ktl, v, vrow, total;
@@ -69,7 +71,9 @@ __host__ __device__ inline PmLds pm_layout(int d_v) {
 }
 
 __device__ __forceinline__ uint32_t bf16_hi(float x) { return f32_to_bf16_bits_rne(x); }
-__device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) { return f32_to_bf16_bits_rne(x - bf16_bits_to_f32(hi)); }
+__device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
+  return f32_to_bf16_bits_rne(x - bf16_bits_to_f32(hi));
+}
 
 // 8 floats -> bf16x8 high and low halves, element j at bits 16 (j % 2) of dword j / 2
 __device__ __forceinline__ void split8(const float (&x)[8], u32x4_t& h, u32x4_t& l) {
@@ -99,10 +103,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_
 }  // namespace
 
 template <int DV>  // columns of S^T per workgroup (d_v, or a 128-column block of it)
-__global__ __launch_bounds__(4 * DV) void prefill_mfma_kernel(const float* __restrict__ kin, const float* __restrict__ vin,
+__global__ __launch_bounds__(4 * DV) void prefill_mfma_kernel(const float* __restrict__ kin,
+                                                              const float* __restrict__ vin,
                                                               const float* __restrict__ ain,
                                                               const float* __restrict__ bin, int H, int N, int d_v,
-                                                              float* __restrict__ sctx_t, float* __restrict__ sctx_out) {
+                                                              float* __restrict__ sctx_t,
+                                                              float* __restrict__ sctx_out) {
   extern __shared__ __align__(16) unsigned char pm_lds[];
   constexpr int kWaves = DV / 16;
   constexpr int kThreads = 4 * DV;
