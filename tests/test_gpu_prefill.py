@@ -76,3 +76,21 @@ def test_prefill_long_every_head():
     cfg = inputs.config(3, R=1, H=4)
     gu.log(f"prefill {cfg.prefill_steps} tokens, R=1 H=4")
     check(cfg, inputs.prefill_inputs(cfg, seed=8))
+
+
+@pytest.mark.parametrize("spread,alpha_lo", [(0.0, 1.0), (0.05, 1.0), (0.05, 0.99), (1.0, 1.0)])
+def test_prefill_correlated_keys_no_decay(spread, alpha_lo):
+    """Keys nearly parallel (k_i = unit(k_0 + spread * noise); spread 0: one key for every token), beta near 1,
+    and no or little decay: the chunked kernel's (I + M) then has its largest off-diagonal entries, and the fp32
+    kernel's state never shrinks.  Both must still follow the float64 recurrence."""
+    for d_v in (128, 96):  # 128: chunked MFMA kernel; 96: row-parallel fp32 kernel
+        cfg = inputs.config(2, R=1, H=2, d_v=d_v, prefill_steps=130)
+        pf = inputs.prefill_inputs(cfg, seed=9)
+        rng = np.random.default_rng(10)
+        k0 = rng.standard_normal((1, 1, cfg.H, cfg.d_k))
+        k = k0 + spread * rng.standard_normal(pf.k.shape)
+        pf.k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+        pf.beta = rng.uniform(0.9, 1.0, size=pf.beta.shape).astype(np.float32)
+        pf.alpha = rng.uniform(alpha_lo, 1.0, size=pf.alpha.shape).astype(np.float32)
+        gu.log(f"prefill, correlated keys (spread {spread}), alpha ~ U({alpha_lo}, 1), d_v={d_v}")
+        check(cfg, pf)
