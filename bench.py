@@ -145,9 +145,9 @@ def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool
     with HIP events on the stream it runs on.  The recurrence is 4 d_k d_v float32 FLOPs per token and head
     (two FMAs per state element), sequential over tokens.  For d_k = 128 and d_v in {16, 32, 64, 128, 256} the
     library runs it in chunked form on the matrix cores: per 32-token chunk and head, G = K K^T (lower 16 x 16
-    blocks, 3 x 16 x 16 x 128 per 128-column block of S^T), Y = K S^T (32 x d_v x 128), U = T X (32 x d_v x 32)
-    and the state update (128 x d_v x 32), each as three bf16 products (high/low halves): that MFMA work against
-    the bf16 peak is the roofline; the rate of the equivalent float32 recurrence is reported beside it."""
+    blocks, 3 x 16 x 16 x 128, once per chunk), Y = K S^T (32 x d_v x 128), U = T X (32 x d_v x 32) and the
+    state update (128 x d_v x 32), each as three bf16 products (high/low halves): that MFMA work against the
+    bf16 peak is the roofline; the rate of the equivalent float32 recurrence is reported beside it."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ctx.prefill(*ctx_in)
     torch.cuda.synchronize()
@@ -163,9 +163,7 @@ def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool
     chunked = cfg.d_k == 128 and cfg.d_v in (16, 32, 64, 128, 256)
     if chunked:
         chunks = -(-N // 32)
-        blocks = max(1, cfg.d_v // 128)
-        per_chunk = 3 * 2.0 * (blocks * 3 * 16 * 16 * 128 + 32 * cfg.d_v * 128 + 32 * cfg.d_v * 32
-                               + 128 * cfg.d_v * 32)
+        per_chunk = 3 * 2.0 * (3 * 16 * 16 * 128 + 32 * cfg.d_v * 128 + 32 * cfg.d_v * 32 + 128 * cfg.d_v * 32)
         mfma_flops = per_chunk * chunks * heads
         roof = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 (high/low halves)",
                 "achieved": mfma_flops / (ms * 1e-3) / 1e12,
@@ -179,7 +177,7 @@ def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool
            "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
            "roofline": roof,
            "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-           "note": "call time: the prefill kernel plus the state's transpose and bf16 split"}
+           "note": "call time: the prefill kernels plus the state's transpose and bf16 split"}
     if with_cpu:
         import oracle
         pf_k = ctx_in[0][:1, :, :1].cpu().numpy()

@@ -135,8 +135,12 @@ onela_status onela_set_context(onela_handle h, const float* d_sctx, void* stream
  * as onela_set_context would ("Scientific Impact Assessment: OneLA", §1: the post-prefill state).
  * d_k: [R][n_tokens][H][d_k], d_v: [R][n_tokens][H][d_v], d_alpha/d_beta: [R][n_tokens][H], all
  * float32.  If d_sctx_out is not NULL the state is also written there as [R][H][d_v][d_k] float32.
- * Any head size the handle accepts (d_k, d_v <= 256); n_tokens = 0 installs the zero state.  The inputs are
- * read once; the work is 4 d_k d_v float32 FLOPs per token and (request, head). */
+ * Any head size the handle accepts (d_k, d_v <= 256); n_tokens = 0 installs the zero state.  The work is
+ * 4 d_k d_v float32 FLOPs per token and (request, head).  The decode state of the workspace (chain tables
+ * and records, or the per-beam states), which a prefill starts afresh, serves as its scratch: with d_k = 128
+ * and d_v in {16, 32, 64, 128, 256} the chunked form keeps 4480 bytes per 32-token chunk and (request, head)
+ * there, in as many passes over the prompt as that space needs, and falls back to a token-by-token float32
+ * recurrence when not even one chunk fits. */
 onela_status onela_prefill(onela_handle h, int32_t n_tokens, const float* d_k, const float* d_v,
                            const float* d_alpha, const float* d_beta, float* d_sctx_out, void* stream);
 

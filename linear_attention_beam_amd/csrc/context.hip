@@ -277,8 +277,10 @@ __global__ __launch_bounds__(LANES * kPfRows) void prefill_kernel(const float* _
 bool prefill_supported(int d_k, int d_v) { return d_k >= 1 && d_k <= 256 && d_v >= 1 && d_v <= 256; }
 
 hipError_t launch_prefill(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
-                          int N, int d_k, int d_v, float* sctx_t, float* sctx_out, hipStream_t s) {
-  if (prefill_mfma_supported(d_k, d_v)) return launch_prefill_mfma(k, v, alpha, beta, R, H, N, d_v, sctx_t, sctx_out, s);
+                          int N, int d_k, int d_v, float* sctx_t, float* sctx_out, void* scratch,
+                          size_t scratch_bytes, hipStream_t s) {
+  if (prefill_mfma_supported(d_k, d_v) && (N == 0 || scratch_bytes >= prefill_mfma_chunk_bytes(R, H)))
+    return launch_prefill_mfma(k, v, alpha, beta, R, H, N, d_v, sctx_t, sctx_out, scratch, scratch_bytes, s);
   const int per4 = (d_k + 31) / 32;
   const int nrb = (d_v + kPfRows - 1) / kPfRows;
   const size_t lds = prefill_lds_bytes(32 * per4);

@@ -38,13 +38,21 @@ hipError_t launch_ancestry(const int32_t* parent, const int32_t* chain_prev, int
 hipError_t launch_clear_flag(int* flag, hipStream_t s);
 hipError_t launch_transpose_sctx(const float* S, float* ST, int RH, int d_v, int d_k, hipStream_t s);
 hipError_t launch_split_frag(const float* ST, uint16_t* frag, int RH, int d_v, int d_k, hipStream_t s);
+// GDN prefill from the zero state into sctx_t ([R][H][d_k][d_v]) and, if not NULL, sctx_out ([R][H][d_v][d_k]).
+// scratch (scratch_bytes, 16-byte aligned, contents not preserved) serves the chunked MFMA form; with less than
+// prefill_mfma_chunk_bytes(R, H) the row-parallel float32 kernel runs instead.
 hipError_t launch_prefill(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
-                          int N, int d_k, int d_v, float* sctx_t, float* sctx_out, hipStream_t s);
+                          int N, int d_k, int d_v, float* sctx_t, float* sctx_out, void* scratch,
+                          size_t scratch_bytes, hipStream_t s);
 bool prefill_supported(int d_k, int d_v);
-// chunked prefill on MFMA (d_k = 128, d_v in {16, 32, 64, 128, 256}); same outputs as launch_prefill
+// chunked prefill on MFMA (d_k = 128, d_v in {16, 32, 64, 128, 256}); same outputs as launch_prefill.  The
+// scratch holds the chunks' T for every (request, head): prefill_mfma_chunk_bytes(R, H) bytes per chunk; longer
+// prompts run in segments of as many chunks as fit.
 bool prefill_mfma_supported(int d_k, int d_v);
+size_t prefill_mfma_chunk_bytes(int R, int H);
 hipError_t launch_prefill_mfma(const float* k, const float* v, const float* alpha, const float* beta, int R, int H,
-                               int N, int d_v, float* sctx_t, float* sctx_out, hipStream_t s);
+                               int N, int d_v, float* sctx_t, float* sctx_out, void* scratch, size_t scratch_bytes,
+                               hipStream_t s);
 
 hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Materializing replay (comparison path): dense parent state rebuilt per pair and step.

@@ -29,6 +29,8 @@ struct onela_ctx {
   float* rec_u;
   float* rec_alpha;
   float* fullstate;
+  unsigned char* scratch;  // the decode state (chains onwards): scratch of onela_prefill, which resets it
+  size_t scratch_bytes;
   bool has_context;
   int t;
   int n_beams;
@@ -205,6 +207,8 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
     h->rec_u = h->rec_alpha = nullptr;
     h->fullstate = reinterpret_cast<float*>(ws + l.fullstate);
   }
+  h->scratch = ws + l.chains;
+  h->scratch_bytes = l.total - l.chains;
   h->has_context = false;
   h->t = 0;
   h->n_beams = 1;
@@ -246,7 +250,7 @@ onela_status onela_prefill(onela_handle h, int32_t n_tokens, const float* d_k, c
     return fail(ONELA_ERR_INVALID_ARG, "prompt too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(launch_prefill(d_k, d_v, d_alpha, d_beta, c.num_requests, c.num_heads, n_tokens, c.d_k, c.d_v,
-                               h->sctx_t, d_sctx_out, s),
+                               h->sctx_t, d_sctx_out, h->scratch, h->scratch_bytes, s),
                 "prefill");
   if (st != ONELA_OK) return st;
   return finish_context(h, s);

@@ -17,9 +17,12 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-4
 
 
-def run_prefill(cfg, pf: inputs.PrefillInputs):
+def run_prefill(cfg, pf: inputs.PrefillInputs, max_beams=8, max_steps=2, qkv_dtype="f32"):
+    """The chunked kernel keeps its per-chunk T in the decode-state part of the workspace, whose size follows
+    max_beams, max_steps and qkv_dtype: the default (8 beams, 2 steps, float32) holds a few chunks per
+    (request, head), so longer prompts run in several segments."""
     dev = gu.device()
-    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, 8, 2, qkv_dtype="f32", device=dev)
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, max_beams, max_steps, qkv_dtype=qkv_dtype, device=dev)
     out = torch.full((cfg.R, cfg.H, cfg.d_v, cfg.d_k), float("nan"), dtype=torch.float32, device=dev)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     ctx.prefill(t(pf.k), t(pf.v), t(pf.alpha), t(pf.beta), sctx_out=out)
@@ -31,8 +34,8 @@ def run_prefill(cfg, pf: inputs.PrefillInputs):
     return got
 
 
-def check(cfg, pf):
-    got = run_prefill(cfg, pf)
+def check(cfg, pf, **ws):
+    got = run_prefill(cfg, pf, **ws)
     ref = oracle.prefill(pf.k, pf.v, pf.alpha, pf.beta)
     assert np.all(np.isfinite(got))
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
@@ -94,3 +97,14 @@ def test_prefill_correlated_keys_no_decay(spread, alpha_lo):
         pf.alpha = rng.uniform(alpha_lo, 1.0, size=pf.alpha.shape).astype(np.float32)
         gu.log(f"prefill, correlated keys (spread {spread}), alpha ~ U({alpha_lo}, 1), d_v={d_v}")
         check(cfg, pf)
+
+
+@pytest.mark.parametrize("max_beams,max_steps,qkv_dtype,what", [
+    (512, 8, "bf16", "one segment"),
+    (1, 1, "f32", "scratch below one chunk: row-parallel fp32 kernel"),
+    (16, 1, "bf16", "segments of one or two chunks"),
+])
+def test_prefill_scratch_sizes(max_beams, max_steps, qkv_dtype, what):
+    cfg = inputs.config(2, R=1, H=2, prefill_steps=200)
+    gu.log(f"prefill 200 tokens, workspace for {max_beams} beams x {max_steps} steps ({qkv_dtype}): {what}")
+    check(cfg, inputs.prefill_inputs(cfg, seed=11), max_beams=max_beams, max_steps=max_steps, qkv_dtype=qkv_dtype)
