@@ -47,6 +47,7 @@ def check(cfg, pf, **ws):
 @pytest.mark.parametrize("d_k,d_v,N", [
     (128, 128, 100), (16, 16, 17), (64, 32, 1), (96, 200, 33), (256, 256, 40), (40, 7, 16), (1, 1, 5),
     (200, 130, 31), (128, 256, 48), (128, 64, 70), (128, 32, 33), (128, 16, 65), (128, 128, 1), (128, 96, 40),
+    (128, 256, 300),
 ])
 def test_prefill_shapes(d_k, d_v, N):
     cfg = inputs.config(2, R=2, H=3, d_k=d_k, d_v=d_v, prefill_steps=N)
