@@ -109,3 +109,41 @@ def test_prefill_scratch_sizes(max_beams, max_steps, qkv_dtype, what):
     cfg = inputs.config(2, R=1, H=2, prefill_steps=200)
     gu.log(f"prefill 200 tokens, workspace for {max_beams} beams x {max_steps} steps ({qkv_dtype}): {what}")
     check(cfg, inputs.prefill_inputs(cfg, seed=11), max_beams=max_beams, max_steps=max_steps, qkv_dtype=qkv_dtype)
+
+
+@pytest.mark.parametrize("mode,generic", [("fullstate", False), ("replay", True), ("replay", False)])
+def test_prefill_then_decode(mode, generic):
+    """The decode after a prefill, in every mode.  The prefill's scratch is the decode state of the workspace
+    (per-beam states for FullState, records and chains otherwise), so the first steps must not see any of it:
+    S matches the oracle prefill, and every head's o (and u, keys, alphas, chains) the oracle decode from it."""
+    cfg = inputs.config(1, R=1, H=4, B=48, L=3, prefill_steps=150)
+    pf = inputs.prefill_inputs(cfg, seed=12)
+    steps = inputs.decode_inputs(cfg)
+    gu.log(f"prefill {cfg.prefill_steps} tokens then {cfg.L} steps, mode={mode} generic={generic}")
+    run = gu.GpuRun(cfg, steps, prefill=pf, mode=mode, force_generic=generic, sctx_out=True)
+    assert run.status == onela.ONELA_OK
+    sctx = run.sctx_gpu.double().cpu().numpy()
+    assert float(np.max(np.abs(sctx - oracle.prefill(pf.k, pf.v, pf.alpha, pf.beta)))) < TOL
+    chains = gu.all_chains(steps, cfg.B, cfg.L, cfg.R)
+    for h in range(cfg.H):
+        ref, _ = gu.oracle_head(sctx[0, h], steps, 0, h, cfg.B, cfg.L)
+        e_o, e_u = gu.compare_head(run, steps, ref, chains[0], 0, h, check_records=mode == "replay")
+        gu.log(f"  head {h}: max|o err|={e_o:.3g} max|u err|={e_u:.3g}")
+    # a second prompt on the same handle: its scratch overwrites the first decode's state, then a new decode
+    pf2 = inputs.prefill_inputs(cfg, seed=13)
+    steps2 = inputs.decode_inputs(cfg, seed=14)
+    dev = gu.device()
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    out = torch.empty((cfg.R, cfg.H, cfg.d_v, cfg.d_k), dtype=torch.float32, device=dev)
+    run.ctx.prefill(t(pf2.k), t(pf2.v), t(pf2.alpha), t(pf2.beta), sctx_out=out)
+    run.outs = [run.ctx.step(**gu.upload_step(s, dev)) for s in steps2]
+    torch.cuda.synchronize()
+    assert run.ctx.status() == onela.ONELA_OK
+    run.view = run.ctx.view()
+    sctx2 = out.double().cpu().numpy()
+    assert float(np.max(np.abs(sctx2 - oracle.prefill(pf2.k, pf2.v, pf2.alpha, pf2.beta)))) < TOL
+    chains2 = gu.all_chains(steps2, cfg.B, cfg.L, cfg.R)
+    for h in range(cfg.H):
+        ref, _ = gu.oracle_head(sctx2[0, h], steps2, 0, h, cfg.B, cfg.L)
+        e_o, e_u = gu.compare_head(run, steps2, ref, chains2[0], 0, h, check_records=mode == "replay")
+        gu.log(f"  second prompt, head {h}: max|o err|={e_o:.3g} max|u err|={e_u:.3g}")
