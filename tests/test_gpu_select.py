@@ -137,3 +137,18 @@ def test_select_all_equal_scores():
     got = run_select(si, 2048)
     assert_same(si, 2048, got)
     assert got[0][0, 0] == 39 and got[1][0, 0] == 499
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_select_random_shapes(i):
+    """A seeded sweep: request count, beams, candidates per beam and survivors drawn at random (survivors up to
+    min(2048, candidates)), half with many exact ties; bit for bit against the oracle."""
+    rng = np.random.default_rng([0x5E1E, i])
+    R = int(rng.integers(1, 6))
+    n_prev = int(rng.choice([1, 2, 3, 17, 64, 128, 255, 512, 1000]))
+    n_cand = int(rng.choice([1, 2, 7, 31, 64, 100, 256, 1024, 3000]))
+    n_beams = int(rng.integers(1, min(2048, n_prev * n_cand) + 1))
+    ties = bool(i % 2)
+    gu.log(f"select random {i}: R={R} n_prev={n_prev} n_cand={n_cand} n_beams={n_beams} ties={ties}")
+    si = inputs.select_inputs(R, n_prev, n_cand, seed=20 + i, ties=ties)
+    assert_same(si, n_beams, run_select(si, n_beams))
