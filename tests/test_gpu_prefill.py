@@ -147,3 +147,21 @@ def test_prefill_then_decode(mode, generic):
         ref, _ = gu.oracle_head(sctx2[0, h], steps2, 0, h, cfg.B, cfg.L)
         e_o, e_u = gu.compare_head(run, steps2, ref, chains2[0], 0, h, check_records=mode == "replay")
         gu.log(f"  second prompt, head {h}: max|o err|={e_o:.3g} max|u err|={e_u:.3g}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_random_shapes(i):
+    """A seeded sweep: requests, heads, head sizes (half on the chunked kernel, d_k = 128), prompt length and
+    the workspace the scratch comes from (so one, several or no chunks per segment), against the oracle."""
+    rng = np.random.default_rng([0x9F11, i])
+    R, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    if i % 2 == 0:
+        d_k, d_v = 128, int(rng.choice([16, 32, 64, 128, 256]))
+    else:
+        d_k, d_v = int(rng.integers(1, 257)), int(rng.integers(1, 257))
+    N = int(rng.integers(0, 400))
+    max_beams, max_steps = int(rng.choice([1, 4, 16, 64])), int(rng.integers(1, 4))
+    qkv = str(rng.choice(["f32", "bf16"]))
+    cfg = inputs.config(2, R=R, H=H, d_k=d_k, d_v=d_v, prefill_steps=N)
+    gu.log(f"prefill random {i}: R={R} H={H} d_k={d_k} d_v={d_v} N={N} workspace {max_beams} x {max_steps} {qkv}")
+    check(cfg, inputs.prefill_inputs(cfg, seed=30 + i), max_beams=max_beams, max_steps=max_steps, qkv_dtype=qkv)
