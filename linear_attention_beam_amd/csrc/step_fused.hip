@@ -17,12 +17,13 @@
 //            as soon as it arrives, with no barrier before it), and writes its own (c_j alpha_b for the
 //            parent's records, 1 for its own record, A alpha_b) for the next step, so no record alpha is
 //            gathered.
-//   Phase 1  the u of the chain records (this lane's 4-row piece of each of its 4 beams) starts streaming
+//   Phase 1  the u of the chain records (this lane's 4-row piece of each of its NB / 16 beams) starts streaming
 //            into a register ring; then 16 lanes per (beam, chain record) take the dot products of the chain
 //            keys with k and q (a ring of kD1 keys per lane), and k . q, reduced with DPP inside a 16-lane
 //            row; append the record key and alpha.
-//   Phase 2  the replay: sum_j c_j (K_j.k) U_j and sum_j c_j (K_j.q) U_j for the 4 beams of this lane,
-//            records-major over a ring of kRM records x 4 tiles.  Then for 16 beams at a time,
+//   Phase 2  the replay: sum_j c_j (K_j.k) U_j and sum_j c_j (K_j.q) U_j for the NB / 16 beams of this
+//            lane, records-major over a ring of kRM records (one when NB = 128 or the chain has one record)
+//            x NB / 16 tiles.  Then for 16 beams at a time,
 //            v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over d_k, high then low half
 //            into one float32 accumulator.  In the accumulator lane l holds beam l % 16 and d_v rows
 //            4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on 16-byte pieces (one
