@@ -16,8 +16,8 @@ Prints one JSON line.  Extra objects:
   hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
-  prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the fp32
-                vector-ALU peak
+  prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the dense
+                bf16 MFMA peak for the chunked kernels (d_k = 128), else the fp32 vector-ALU peak
   stack         a whole beam-search decode through several GDN layers with random weights (projections as
                 library GEMMs, one decode context per layer, the GPU beam selection between steps) at the
                 workload's R, H, B, L and head sizes; context for the step's share of a model's decode
