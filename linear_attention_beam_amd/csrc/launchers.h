@@ -18,15 +18,13 @@ struct StepArgs {
   const float* sctx_t;    // [R][H][d_k][d_v]
   const uint16_t* sctx_frag;  // bf16 high/low MFMA fragments of S_ctx (fused kernel only)
   void* rec_k;            // [R][H][slots][d_k] input dtype
-  float* rec_u;           // fused kernel: [R][H] tiles of u_slots16(slots) x u_rows16(d_v) (u_index); others [R][H][slots][d_v]
+  float* rec_u;           // [R][H][slots][d_v]
   float* rec_alpha;       // [R][H][slots]
   const int32_t* chain;   // chain table after this step, [R][B_max][L_max] (read by the generic kernel)
   // ancestry inputs (the fused kernel derives chains itself and writes the new table)
   const int32_t* parent;      // [R][n]
   const int32_t* chain_prev;  // table after step t-1, NULL at t = 1
   int32_t* chain_out;         // table after step t
-  const float* decay_prev;    // fused kernel: [R][H][B_max][L_max + 1] decays along each chain after step t-1
-  float* decay_out;           //   (c_0 .. c_{L_max-1}, then A); this step's rows
   int* flag;                  // set to `epoch` when a parent index is out of range
   int epoch;
   int b_prev;
@@ -58,11 +56,15 @@ hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Materializing replay (comparison path): dense parent state rebuilt per pair and step.
 hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t s);
 
-// Fused bf16-MFMA step (d_k == 128, d_v % 32 == 0, d_v <= 256).  tile_beams 0 = automatic.
+// Fused bf16-MFMA step (d_k == 128, d_v % 32 == 0, 32 <= d_v <= 256, L_max <= 64), tiles of 16 or 32 beams.
+// Steps t >= 2 first run the ancestry-plan kernel, which writes the chain table and per-tile plans into `plan`
+// (fused_plan_bytes).  fused_prepare sets the kernel's LDS limit and returns its persistent grid size.
 bool fused_supported(int d_k, int d_v, int L_max);
-int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested);
+int fused_pick_tile(int d_v, int L_max, int requested);
 size_t fused_lds_bytes(int tile, int L_max, int d_v);
-hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s);
+size_t fused_plan_bytes(int R, int B_max, int L_max);
+hipError_t fused_prepare(int tile, int d_v, int L_max, int* grid);
+hipError_t launch_step_fused(const StepArgs& a, int tile, void* plan, int grid, hipStream_t s);
 
 // Beam selection: top n_beams of beam_score + logp per request, best first (beam_select.hip).
 int beam_select_max_beams();

@@ -24,7 +24,9 @@ struct onela_ctx {
   float* sctx_t;
   uint16_t* sctx_frag;
   int32_t* chains;
-  float* decay;  // fused path: [2][R][H][B_max][L_max + 1], step t writes buffer t % 2
+  unsigned char* plan;  // fused path: per (request, beam tile) ancestry plans of the current step
+  int tile;      // fused path: beams per tile
+  int grid;      // fused path: persistent workgroups (compute units x workgroups per unit)
   void* rec_k;
   float* rec_u;
   float* rec_alpha;
@@ -58,7 +60,7 @@ onela_status ok() {
 }
 
 struct Layout {
-  size_t flag, sctx_t, sctx_frag, chains, decay, rec_k, rec_u, rec_alpha, fullstate, total;
+  size_t flag, sctx_t, sctx_frag, chains, plan, rec_k, rec_u, rec_alpha, fullstate, total;
   bool fused;
 };
 
@@ -81,9 +83,8 @@ onela_status check_config(const onela_config* c) {
     return fail(ONELA_ERR_INVALID_ARG, "mode %d is not REPLAY or FULLSTATE", c->mode);
   if (c->flags & ~(ONELA_FLAG_FORCE_GENERIC | ONELA_FLAG_MATERIALIZE))
     return fail(ONELA_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
-  if (c->tile_beams != 0 && c->tile_beams != 16 && c->tile_beams != 32 && c->tile_beams != 64 &&
-      c->tile_beams != 128)
-    return fail(ONELA_ERR_INVALID_ARG, "tile_beams %d is not 0, 16, 32, 64 or 128", c->tile_beams);
+  if (c->tile_beams != 0 && c->tile_beams != 16 && c->tile_beams != 32)
+    return fail(ONELA_ERR_INVALID_ARG, "tile_beams %d is not 0, 16 or 32", c->tile_beams);
   const double slots_total =
       (double)c->num_requests * c->num_heads * (double)c->max_beams * c->max_steps * (c->d_k + c->d_v);
   if (slots_total > 9.0e15) return fail(ONELA_ERR_INVALID_ARG, "configuration too large");
@@ -108,12 +109,10 @@ Layout make_layout(const onela_config* c) {
   l.sctx_t = off;     off = align256(off + R * H * dk * dv * 4);
   l.sctx_frag = off;  off = align256(off + (l.fused ? R * H * dk * dv * 2 * 2 : 0));
   l.chains = off;     off = align256(off + L * R * B * L * 4);
-  l.decay = off;      off = align256(off + (l.fused ? 2 * R * H * B * (L + 1) * 4 : 0));
+  l.plan = off;       off = align256(off + (l.fused ? fused_plan_bytes((int)R, (int)B, (int)L) : 0));
   if (c->mode == ONELA_MODE_REPLAY) {
     l.rec_k = off;     off = align256(off + R * H * slots * dk * in_bytes);
-    // the fused kernel keeps u in 16 x 16 tiles of (slot, row), padded to multiples of 16; the others row by row
-    l.rec_u = off;     off = align256(off + (l.fused ? R * H * ((slots + 15) / 16 * 16) * ((dv + 15) / 16 * 16) * 4
-                                                     : R * H * slots * dv * 4));
+    l.rec_u = off;     off = align256(off + R * H * slots * dv * 4);
     l.rec_alpha = off; off = align256(off + R * H * slots * 4);
     l.fullstate = 0;
   } else {
@@ -196,7 +195,23 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
   h->sctx_t = reinterpret_cast<float*>(ws + l.sctx_t);
   h->sctx_frag = l.fused ? reinterpret_cast<uint16_t*>(ws + l.sctx_frag) : nullptr;
   h->chains = reinterpret_cast<int32_t*>(ws + l.chains);
-  h->decay = l.fused ? reinterpret_cast<float*>(ws + l.decay) : nullptr;
+  h->plan = l.fused ? ws + l.plan : nullptr;
+  h->tile = 0;
+  h->grid = 0;
+  if (l.fused) {
+    h->tile = fused_pick_tile(cfg->d_v, cfg->max_steps, cfg->tile_beams);
+    const size_t lds = fused_lds_bytes(h->tile, cfg->max_steps, cfg->d_v);
+    if (lds > (size_t)max_lds) {
+      delete h;
+      return fail(ONELA_ERR_UNSUPPORTED, "tile_beams %d with max_steps %d needs %zu bytes of LDS, the device allows %d",
+                  h->tile, cfg->max_steps, lds, max_lds);
+    }
+    const hipError_t e = fused_prepare(h->tile, cfg->d_v, cfg->max_steps, &h->grid);
+    if (e != hipSuccess) {
+      delete h;
+      return fail(ONELA_ERR_DEVICE, "fused kernel set-up: %s", hipGetErrorString(e));
+    }
+  }
   if (cfg->mode == ONELA_MODE_REPLAY) {
     h->rec_k = ws + l.rec_k;
     h->rec_u = reinterpret_cast<float*>(ws + l.rec_u);
@@ -268,13 +283,6 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
     return fail(ONELA_ERR_INVALID_ARG, "n_beams (%d) must be in 1..max_beams (%d)", n_beams, c.max_beams);
   if (!d_q || !d_k || !d_v || !d_alpha || !d_beta || !d_parent_idx || !d_o)
     return fail(ONELA_ERR_INVALID_ARG, "a step buffer is NULL");
-  int tile = 0;
-  if (c.mode == ONELA_MODE_REPLAY && h->fused) {
-    tile = fused_pick_tile(c.num_requests, c.num_heads, n_beams, c.d_v, c.max_steps, c.tile_beams);
-    if (fused_lds_bytes(tile, c.max_steps, c.d_v) > (size_t)h->max_lds)
-      return fail(ONELA_ERR_UNSUPPORTED, "tile_beams %d with max_steps %d needs %zu bytes of LDS, the device allows %d",
-                  tile, c.max_steps, fused_lds_bytes(tile, c.max_steps, c.d_v), h->max_lds);
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = h->t + 1;
   const size_t table = (size_t)c.num_requests * c.max_beams * c.max_steps;
@@ -295,11 +303,6 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
   a.chain = chain_out;
   a.parent = d_parent_idx; a.chain_prev = chain_prev; a.chain_out = chain_out;
   a.flag = h->flag; a.epoch = h->epoch; a.b_prev = h->n_beams;
-  if (h->decay) {
-    const size_t dbuf = (size_t)c.num_requests * c.num_heads * c.max_beams * (c.max_steps + 1);
-    a.decay_prev = h->decay + (size_t)((t - 1) & 1) * dbuf;
-    a.decay_out = h->decay + (size_t)(t & 1) * dbuf;
-  }
   a.R = c.num_requests; a.H = c.num_heads; a.d_k = c.d_k; a.d_v = c.d_v; a.n = n_beams;
   a.B_max = c.max_beams; a.L_max = c.max_steps; a.slots = c.max_beams * c.max_steps; a.t = t;
   const bool bf16 = c.qkv_dtype == ONELA_BF16;
@@ -309,7 +312,7 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
     float* next = h->fullstate + (size_t)(t & 1) * buf;
     st = launched(launch_fullstate(a, bf16, d_parent_idx, h->n_beams, prev, next, s), "FullState step");
   } else if (h->fused) {
-    st = launched(launch_step_fused(a, tile, s), "fused step");
+    st = launched(launch_step_fused(a, h->tile, h->plan, h->grid, s), "fused step");
   } else {
     st = h->materialize ? launched(launch_step_materialize(a, bf16, s), "materializing step")
                         : launched(launch_step_generic(a, bf16, s), "step");

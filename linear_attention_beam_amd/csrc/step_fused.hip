@@ -1,40 +1,32 @@
-// Fused projection-replay decode step for gfx950: ancestry update, bf16 MFMA contraction of the shared
-// state, record replay and record append in one kernel ("Scientific Impact Assessment: OneLA", §1: a fused
-// GPU kernel reuses S_ctx across beams; paper index page, Abstract).
+// Fused projection-replay decode step for gfx950 ("Scientific Impact Assessment: OneLA", §1: a fused GPU
+// kernel reuses S_ctx across beams; paper index page, Abstract).  Two launches per step (one at step 1):
 //
-// Workgroup = (request, head, tile of NB beams), or a run of consecutive tiles of one (request, head) when
-// the register file admits a single workgroup per CU; d_v / 16 waves of 64 lanes (d_k = 128 fixed).
-//   Phase 0  everything that needs nothing from the ancestry goes out in the first round trip: parents,
-//            alpha and beta; k, q and v rows of the tile (16-byte loads, held in registers and written to
-//            LDS only after the chain rows are requested, so that the two round trips overlap); this
-//            wave's S_ctx rows.  Wave w owns d_v rows 16w .. 16w+15 of S_ctx, whose bf16 high and low halves stay
-//            in registers for the whole tile (each S_ctx element is read once per tile and reused by all
-//            NB beams).  Then the ancestry index ("Scientific Impact Assessment: OneLA", §1 item (3)): each
-//            beam's chain is its parent's chain from the previous table plus its own slot; the head-0
-//            workgroups write the new table.  The decays along a chain (A = prod alpha, c_j = prod of the
-//            alphas after record j) are kept per (request, head, beam) next to the index: a beam reads its
-//            parent's row (chain entries and A in one round trip, issued by the thread that holds the parent
-//            as soon as it arrives, with no barrier before it), and writes its own (c_j alpha_b for the
-//            parent's records, 1 for its own record, A alpha_b) for the next step, so no record alpha is
-//            gathered.
-//   Phase 1  the u of the chain records (this lane's 4-row piece of each of its NB / 16 beams) starts streaming
-//            into a register ring; then 16 lanes per (beam, chain record) take the dot products of the chain
-//            keys with k and q (a ring of kD1 keys per lane), and k . q, reduced with DPP inside a 16-lane
-//            row; append the record key and alpha.
-//   Phase 2  the replay: sum_j c_j (K_j.k) U_j and sum_j c_j (K_j.q) U_j for the NB / 16 beams of this
-//            lane, records-major over a ring of kRM records (one when NB = 128 or the chain has one record)
-//            x NB / 16 tiles.  Then for 16 beams at a time,
-//            v_mfma_f32_16x16x32_bf16 computes [P_k | P_q]^T = S_rows [k | q] over d_k, high then low half
-//            into one float32 accumulator.  In the accumulator lane l holds beam l % 16 and d_v rows
-//            4 (l / 16) .. +3 of the wave's 16 rows, so the replay works per beam on 16-byte pieces (one
-//            float4 load of each chain record's u) and u and o leave as float4 stores:
-//              p = A P_k + sum_j c_j (K_j.k) U_j,  u = beta (v - alpha p),
-//              o = alpha (A P_q + sum_j c_j (K_j.q) U_j) + (k.q) u.
-//   Every gather of phases 1 and 2 is an unconditional load in a software pipeline (indices past the end
-//   are clamped to a valid record and the values dropped): the compiler's waits on the in-order vmcnt then
-//   cover exactly the load consumed, not the loads and stores issued after it.
-// Workgroups of one (request, head) are mapped to the same XCD (dispatch is round-robin over the 8 XCDs)
-// so their S_ctx reads share one L2.
+// ancestry_plan_kernel (steps t >= 2), one workgroup per request.
+//   * The ancestry index (review §1 item (3)): each beam's chain is its parent's chain from the previous table
+//     plus its own slot; the kernel writes the new table.
+//   * A processing order: the beams sorted by their history (a counting sort on the parent's place in the
+//     previous step's order, which keeps the whole chains in lexicographic order).  Beams with common
+//     ancestors then share tiles, so a tile touches few distinct records and neighbouring tiles share the rest.
+//     The order only decides which workgroup computes which beam: every output lands at its beam's place.
+//   * One plan per tile of NB consecutive beams in that order, shared by every head (slots are the same for
+//     all heads): the beams, the distinct ancestor slots (chain position by chain position, in order of first
+//     appearance) and, for each beam and chain position, the place of its record in that list.
+//
+// step_fused_kernel, persistent: a workgroup walks a list of jobs (request, head, block of RB rows of d_v, run
+//   of beam tiles); two workgroups share a compute unit.  Wavefront w owns d_v rows RB*rb + 16w .. +15 of
+//   S_ctx, whose bf16 high and low halves stay in registers for the whole job (S_ctx is read once per job and
+//   reused by every beam of every tile of the job).  Per tile:
+//   * one round trip brings everything into LDS: the beams' k, q and v rows (16-byte loads through registers),
+//     and, copied straight into LDS (global_load_lds), the keys, alphas and u rows of the tile's distinct
+//     ancestor records, the beams and the plan places.  The plan itself was loaded during the previous tile;
+//   * 16 lanes per beam walk its chain newest to oldest, taking the dot products of the record keys with k and
+//     q, scaled by the decay product c_j of the alphas after record j (four records at a time);
+//   * per 16 beams, v_mfma_f32_16x16x32_bf16 forms [P_k | P_q]^T = S_rows [k | q], high then low half into one
+//     float32 accumulator; in the accumulator lane l holds beam l % 16 and d_v rows 4 (l / 16) .. +3 of the
+//     wavefront's 16 rows, so the replay works per beam on 16-byte pieces of u, and u and o leave as float4:
+//       p = A P_k + sum_j c_j (K_j . k) U_j,   u = beta (v - alpha p),
+//       o = alpha (A P_q + sum_j c_j (K_j . q) U_j) + (k . q) u,        A = prod_j alpha_j.
+//   A tile whose distinct records do not fit in LDS reads them from memory instead (same arithmetic).
 #include <algorithm>
 
 #include "device_common.h"
@@ -43,479 +35,634 @@
 namespace onela {
 
 namespace {
-constexpr int kDK = 128;             // d_k of the fused kernel
-constexpr int kKS = kDK / 32;        // MFMA k-steps
-constexpr int kXRow = 2 * kDK + 16;  // bytes per staged key/query row (padded against bank conflicts)
-constexpr int kD1 = 4;               // chain keys in flight per lane (phase 1)
-constexpr int kRM = 2;               // chain records per tile in flight per lane (phase 2)
-constexpr int kChainChunk = 8;      // chain entries per round trip of the parent-row reads
-constexpr int kPersistTiles = 4;     // tiles per workgroup when one workgroup fills a CU
+constexpr int kDK = 128;        // d_k of the fused kernel
+constexpr int kKS = kDK / 32;   // MFMA k-steps
+constexpr int kRow = 2 * kDK;   // bytes per k or q row (bf16)
+constexpr int kCap = 64;        // distinct ancestor records of a tile staged in LDS (beyond: read from memory)
+constexpr int kSort = 2048;     // beams per request the plan kernel sorts (more: they keep their own order)
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+
+// Plan record of one (request, tile), in bytes: nd, the distinct slots (up to kCap), the NB beams (padded with
+// the last beam), then one byte per (beam, chain position): the place of its record in the distinct list.
+struct PlanLayout {
+  int perm, li, bytes;
 };
-constexpr int kPX = 4;               // 16-byte pieces of the k and q rows per thread held in registers
-constexpr int kPV = 2;               // 16-byte pieces of the v rows per thread held in registers
-
-struct FusedLds {
-  int xs, slot, alph, coef, item, beamA, beamAl, beamBe, beamKq, vs, vrow, total;
-};
-
-// Per-beam tables use an odd row stride so that 16 beams read by one wave fall in distinct LDS banks.
-__host__ __device__ inline int table_stride(int L) { return L | 1; }
-
-__host__ __device__ inline FusedLds fused_layout(int NB, int L, int d_v) {
-  const int LS = table_stride(L);
-  FusedLds l;
-  int off = 0;
-  l.xs = off;      off += 2 * NB * kXRow;  // k rows, then q rows
-  l.slot = off;    off += NB * LS * 4;     // chain slots
-  l.alph = off;    off += NB * LS * 4;     // c_j
-  l.coef = off;    off += NB * LS * 8;     // (c_j (K_j . k), c_j (K_j . q)) pairs
-  l.item = off;    off += NB * L * 8;      // phase-1 work list: (slot, bb << 16 | bb * LS + m)
-  l.beamA = off;   off += NB * 4;
-  l.beamAl = off;  off += NB * 4;
-  l.beamBe = off;  off += NB * 4;
-  l.beamKq = off;  off += NB * 4;
-  l.vrow = d_v * 2 + 16;
-  l.vs = off;      off += NB * l.vrow;     // v rows (bf16, padded like the k and q rows)
-  l.total = off;
-  return l;
+__host__ __device__ inline PlanLayout plan_layout(int NB, int L) {
+  PlanLayout p;
+  p.perm = align16(4 + 4 * kCap);
+  p.li = p.perm + NB * 4;
+  p.bytes = p.li + align16(NB * L);
+  return p;
 }
-// LDS a workgroup may take without LDS cutting the VGPR-limited occupancy (4 waves per SIMD, 16 per CU):
-// 160 KB per CU shared by 16 / (d_v / 16) workgroups.
-inline size_t lds_budget(int d_v) { return (size_t)640 * d_v; }
+
+// LDS layout of one tile.
+struct FusedLds {
+  int xk, xq, xv, al, be, pm, li, kd, ud, ad, coef, beamA, beamKq, total;
+};
+__host__ __device__ inline int coef_stride(int L) { return L | 1; }  // odd: 16 beams in distinct banks
+__host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB) {
+  FusedLds y;
+  int o = 0;
+  y.xk = o;  o += NB * kRow;               // k rows, 16-byte pieces swizzled by row
+  y.xq = o;  o += NB * kRow;               // q rows
+  y.xv = o;  o += NB * RB * 2;             // this row block of the v rows, swizzled
+  y.al = o;  o += align16(NB * 4);
+  y.be = o;  o += align16(NB * 4);
+  y.pm = o;  o += align16(NB * 4);         // the tile's beams
+  y.li = o;  o += align16(NB * L);         // place of each chain record in the distinct list
+  y.kd = o;  o += kCap * kRow;             // keys of the distinct records
+  y.ud = o;  o += kCap * RB * 4;           // their u rows of this row block, 16-byte pieces swizzled by record
+  y.ad = o;  o += align16(kCap * 4);       // their alphas at this head
+  y.coef = o;   o += NB * coef_stride(L) * 8;
+  y.beamA = o;  o += align16(NB * 4);
+  y.beamKq = o; o += align16(NB * 4);
+  y.total = o;
+  return y;
+}
+
+// Rows of d_v per job: the largest of 128, 64, 32 that divides d_v.
+__host__ __device__ inline int row_block(int d_v) { return d_v % 128 == 0 ? 128 : (d_v % 64 == 0 ? 64 : 32); }
+
+// Job schedule: job j = (request, head, row block, run of tiles).  Jobs of one (request, head) are congruent
+// modulo 8, so with a grid that is a multiple of 8 they run on one XCD (dispatch is round-robin over 8) and
+// share its L2 for the head's records.
+struct Sched {
+  int RH, NRB, ntile, TJ, JPR, njobs;
+};
+inline Sched make_sched(int RH, int NRB, int ntile, int grid) {
+  Sched s;
+  s.RH = RH;
+  s.NRB = NRB;
+  s.ntile = ntile;
+  const long total = (long)RH * NRB * ntile;
+  s.TJ = (int)std::max(1L, std::min((long)ntile, total / std::max(grid, 1)));
+  s.JPR = (ntile + s.TJ - 1) / s.TJ;
+  s.njobs = RH * NRB * s.JPR;
+  return s;
+}
+struct Job {
+  int rh, rb, t0, t1;
+};
+__device__ inline Job job_of(const Sched& s, int j) {
+  Job q;
+  int rem;
+  const int per = s.NRB * s.JPR;
+  if ((s.RH & 7) == 0) {
+    const int x = j & 7, y = j >> 3;
+    q.rh = (y / per) * 8 + x;
+    rem = y - (y / per) * per;
+  } else {
+    q.rh = j / per;
+    rem = j - q.rh * per;
+  }
+  q.rb = rem / s.JPR;
+  const int jr = rem - q.rb * s.JPR;
+  q.t0 = jr * s.TJ;
+  q.t1 = min(s.ntile, q.t0 + s.TJ);
+  return q;
+}
+
+// Cursor over a workgroup's (job, tile) sequence.
+struct Cursor {
+  int job, tile;
+  Job J;
+  bool valid;
+};
+__device__ inline Cursor cursor_first(const Sched& s) {
+  Cursor c;
+  c.job = blockIdx.x;
+  c.valid = c.job < s.njobs;
+  c.tile = 0;
+  if (c.valid) {
+    c.J = job_of(s, c.job);
+    c.tile = c.J.t0;
+  }
+  return c;
+}
+__device__ inline Cursor cursor_next(const Sched& s, Cursor c) {
+  if (!c.valid) return c;
+  if (c.tile + 1 < c.J.t1) {
+    c.tile += 1;
+    return c;
+  }
+  c.job += gridDim.x;
+  c.valid = c.job < s.njobs;
+  if (c.valid) {
+    c.J = job_of(s, c.job);
+    c.tile = c.J.t0;
+  }
+  return c;
+}
+
+// Copies 16 (or 4) bytes per active lane from memory straight into LDS: lane l writes dst + 16 l (4 l); dst is
+// the same for the whole wavefront.
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 4, 0, 0);
+}
+
+// Inclusive prefix sum over a wavefront.
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
 }  // namespace
 
-template <int NB, bool PERSIST>
-__global__ __launch_bounds__(1024) void step_fused_kernel(StepArgs a, int ntile, int tps) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v;
-  const int LS = table_stride(L);
-  const FusedLds lay = fused_layout(NB, L, d_v);
-  const int nthreads = blockDim.x;
-
-  // ---- workgroup -> (request, head, run of tps consecutive tiles); workgroups of one (request, head) share
-  // an XCD ----
-  const int nsplit = (ntile + tps - 1) / tps;
-  int rh, split;
-  if (((a.R * H) & 7) == 0) {
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    rh = (j / nsplit) * 8 + x;
-    split = j - (j / nsplit) * nsplit;
-  } else {
-    rh = blockIdx.x / nsplit;
-    split = blockIdx.x - rh * nsplit;
-  }
-  const int r = rh / H, h = rh - r * H;
-  const int nch = a.t - 1;
-  const size_t arena = (size_t)rh * a.slots;
-  // S_ctx rows of a wave.  Fragment file per (request, head): [hl][w][ks][mi][lane][8], rows
-  // 32 w + 16 mi + lane % 16; wave x takes the block w = x / 2, mi = x % 2.  Wave w owns d_v rows
-  // 16w .. 16w+15; their bf16 high and low halves stay in registers while the workgroup runs.
-  bf16x8_t sf[kKS][2];
-  auto load_sf = [&](int wave, int lane) {
-    const int W = d_v / 32;
-    const size_t half = (size_t)W * kKS * 2 * 64;  // fragments per half
-    const u32x4_t* __restrict__ fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl)
-        sf[ks][hl] = __builtin_bit_cast(
-            bf16x8_t, fr[hl * half + (((size_t)(wave >> 1) * kKS + ks) * 2 + (wave & 1)) * 64 + lane]);
+// ---------------------------------------------------------------------------------------------------------
+// Ancestry index, processing order and tile plans for step t >= 2 (see the top of the file).  rank[r][b]: the
+// place of beam b in its request's processing order, written for the next step.
+// ---------------------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigned char* __restrict__ plan,
+                                                             int plan_bytes, int perm_off, int li_off,
+                                                             int* __restrict__ rank) {
+  static_assert(NB <= 64, "one lane per beam of a tile");
+  __shared__ int s_par[kSort];
+  __shared__ int s_key[kSort];
+  __shared__ int s_perm[kSort];
+  __shared__ int s_cnt[kSort + 1];
+  const int L = a.L_max, n = a.n, t = a.t, nch = t - 1;
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
+  const int ntile = (n + NB - 1) / NB;
+  const bool sorted = n <= kSort && a.b_prev <= kSort;
+  const int* parent = a.parent + (size_t)r * n;
+  auto parent_of = [&](int b) {  // range-checked: a bad index raises the sticky flag and becomes 0
+    int p = parent[b];
+    if (p < 0 || p >= a.b_prev) {
+      *a.flag = a.epoch;
+      p = 0;
+    }
+    return p;
   };
-
-  auto do_tile = [&](const int tile, const int tid) {
-    unsigned char* xs = lds + lay.xs;
-    unsigned char* vs = lds + lay.vs;
-    int* slot_tab = reinterpret_cast<int*>(lds + lay.slot);
-    float* c_tab = reinterpret_cast<float*>(lds + lay.alph);
-    f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
-    int2* item_tab = reinterpret_cast<int2*>(lds + lay.item);
-    float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
-    float* beamAl = reinterpret_cast<float*>(lds + lay.beamAl);
-    float* beamBe = reinterpret_cast<float*>(lds + lay.beamBe);
-    float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
-    const int lane = tid & 63, wave = tid >> 6;
-    const int b0 = tile * NB;
-    const int nb = min(NB, n - b0);
-    // Uniform per-workgroup bases; per-lane offsets are 32-bit (the host checks that they fit).
-    const size_t row0 = ((size_t)r * n + b0) * H + h;  // input row of beam b0 at this head
-    const uint16_t* __restrict__ qin = static_cast<const uint16_t*>(a.q) + row0 * kDK;
-    const uint16_t* __restrict__ kin = static_cast<const uint16_t*>(a.k) + row0 * kDK;
-    const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(a.v) + row0 * d_v;
-    float* __restrict__ o_wr = a.o + row0 * d_v;
-    const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs
-    // Records are read only at slots of earlier steps and written only at this step's slots, so the read
-    // and write views never touch the same element.
-    const uint16_t* __restrict__ k_rd = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
-    uint16_t* __restrict__ k_wr = static_cast<uint16_t*>(a.rec_k) + arena * kDK;
-    // u arena of this (request, head); d_v is a multiple of 32 here, so d_v16 = d_v
-    const size_t u_arena = (size_t)rh * u_slots16(a.slots) * d_v;
-    const float* __restrict__ u_rd = a.rec_u + u_arena;
-    float* __restrict__ u_wr = a.rec_u + u_arena;
-    float* __restrict__ al_wr = a.rec_alpha + arena;
-    auto in_row = [&](int bb) { return row0 + (size_t)bb * H; };
-
-    // ---- phase 0: parents, alpha, beta; k, q and v into LDS; the S_ctx rows into registers.  Every load
-    // goes out before the first value is used: thread tid < NB keeps beam tid's parent, alpha and beta in
-    // registers until the k, q, v and S_ctx requests have been issued (nthreads = 4 d_v >= NB). ----
-    // loads are issued unconditionally (clamped indices, values dropped afterwards) so that the compiler can
-    // count them exactly and later waits do not cover loads issued after the one they need
-    const int tb = min(tid, nb - 1);
-    int pP = a.parent[(size_t)r * n + b0 + tb];
-    float pAl = a.alpha[in_row(tb)];
-    float pBe = a.beta[in_row(tb)];
-    __builtin_amdgcn_sched_barrier(0);  // keep these first in issue order
-    // k, q and v of the tile go to registers now and to LDS only after the chain rows are requested, so
-    // the chain round trip overlaps this one
-    const int vc = d_v >> 3;  // 16-byte pieces per v row
-    auto x_piece = [&](int idx) -> u32x4_t {  // idx < NB * 32; rows < NB are keys, the others queries
-      const int row = idx >> 4, c = idx & 15;
-      const int bb = row < NB ? row : row - NB;
-      u32x4_t val = *reinterpret_cast<const u32x4_t*>((row < NB ? kin : qin) + (unsigned)min(bb, nb - 1) * hk + c * 8);
-      if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
-      return val;
-    };
-    auto v_piece = [&](int idx) -> u32x4_t {  // idx < NB * vc
-      const int bb = idx / vc, c = idx - bb * vc;
-      u32x4_t val = *reinterpret_cast<const u32x4_t*>(vin + (unsigned)min(bb, nb - 1) * hv + c * 8);
-      if (bb >= nb) val = (u32x4_t){0u, 0u, 0u, 0u};
-      return val;
-    };
-    u32x4_t XR[kPX], VR[kPV];
-#pragma unroll
-    for (int u = 0; u < kPX; ++u) XR[u] = x_piece(min(tid + u * nthreads, NB * 32 - 1));
-#pragma unroll
-    for (int u = 0; u < kPV; ++u) VR[u] = v_piece(min(tid + u * nthreads, NB * vc - 1));
-    auto store_x = [&]() {
-#pragma unroll
-      for (int u = 0; u < kPX; ++u) {
-        const int idx = tid + u * nthreads;
-        if (idx < NB * 32) *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = XR[u];
-      }
-      for (int idx = tid + kPX * nthreads; idx < NB * 32; idx += nthreads)
-        *reinterpret_cast<u32x4_t*>(xs + (idx >> 4) * kXRow + (idx & 15) * 16) = x_piece(idx);
-#pragma unroll
-      for (int u = 0; u < kPV; ++u) {
-        const int idx = tid + u * nthreads;
-        if (idx < NB * vc) {
-          const int bb = idx / vc;
-          *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = VR[u];
-        }
-      }
-      for (int idx = tid + kPV * nthreads; idx < NB * vc; idx += nthreads) {
-        const int bb = idx / vc;
-        *reinterpret_cast<u32x4_t*>(vs + bb * lay.vrow + (idx - bb * vc) * 16) = v_piece(idx);
-      }
-    };
-    const int gq = lane >> 4, col = lane & 15;
-    const int dv0 = wave * 16 + 4 * gq;  // this lane's d_v rows: dv0 .. dv0+3
-    constexpr int kTiles = NB / 16;
-    if constexpr (!PERSIST) load_sf(wave, lane);
-    __builtin_amdgcn_sched_barrier(0);  // every streaming request is out before the parents are consumed
-    if (tid >= nb) {
-      pP = 0;
-      pAl = 0.f;
-      pBe = 0.f;
-    }
-    // ---- phase 0 (cont.): thread tid < NB holds beam tid's parent and reads the parent's chain row and decay
-    // row itself, as soon as the parent has arrived (no barrier before this round trip); this step's rows.
-    // Loads are unconditional (entries past the chain are clamped to its last one and dropped). ----
-    const int drow = L + 1;  // decay row: c_0 .. c_{L-1}, then A
-    if (tid < NB) {
-      // sticky flag; decode as a child of beam 0 so that accesses stay in bounds
-      if (tid < nb && (pP < 0 || pP >= a.b_prev)) {
-        *a.flag = a.epoch;
-        pP = 0;
-      }
-      beamAl[tid] = pAl;
-      beamBe[tid] = pBe;
-      const bool live = tid < nb;
-      float* dout = a.decay_out + ((size_t)rh * a.B_max + b0 + tid) * drow;
-      int32_t* cout = a.chain_out + ((size_t)r * a.B_max + b0 + tid) * L;
-      if (nch > 0) {
-        const int32_t* crow = a.chain_prev + ((size_t)r * a.B_max + pP) * L;
-        const float* drw = a.decay_prev + ((size_t)rh * a.B_max + pP) * drow;
-        const float Ap = drw[L];
-        for (int m0 = 0; m0 < nch; m0 += kChainChunk) {
-          int raw[kChainChunk];
-          float dec[kChainChunk];
-#pragma unroll
-          for (int u = 0; u < kChainChunk; ++u) {
-            const int m = min(m0 + u, nch - 1);
-            raw[u] = crow[m];
-            dec[u] = drw[m];
-          }
-#pragma unroll
-          for (int u = 0; u < kChainChunk; ++u) {
-            const int m = m0 + u;
-            if (live && m < nch) {
-              const int sl = raw[u] < 0 ? 0 : (raw[u] >= a.slots ? a.slots - 1 : raw[u]);
-              slot_tab[tid * LS + m] = sl;
-              c_tab[tid * LS + m] = dec[u];
-              item_tab[tid * nch + m] = make_int2(sl, (tid << 16) | (tid * LS + m));
-              dout[m] = dec[u] * pAl;
-              if (h == 0) cout[m] = raw[u];
-            }
-          }
-        }
-        if (live) {
-          dout[nch] = 1.f;
-          dout[L] = Ap * pAl;
-        }
-        beamA[tid] = live ? Ap : 0.f;
-      } else {
-        if (live) {
-          dout[0] = 1.f;
-          dout[L] = pAl;
-        }
-        beamA[tid] = live ? 1.f : 0.f;
-      }
-      if (h == 0 && live) {  // the rest of the row: own slot, then -1
-        for (int m = nch; m < L; ++m) cout[m] = m == nch ? nch * a.B_max + b0 + tid : -1;
-      }
-    }
-    if (h == 0 && tile == ntile - 1) {  // rows of beams >= n are all -1
-      for (int idx = tid; idx < (a.B_max - n) * L; idx += nthreads)
-        a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
-    }
-    store_x();
+  if (sorted) {
+    for (int k = tid; k <= a.b_prev; k += nt) s_cnt[k] = 0;
     __syncthreads();
+    for (int b = tid; b < n; b += nt) {
+      const int p = parent_of(b);
+      s_par[b] = p;
+      // the parent's place in the previous step's order (step 1 has a single beam)
+      const int key = nch == 1 ? p : rank[(size_t)r * a.B_max + p];
+      s_key[b] = key;
+      atomicAdd(&s_cnt[key + 1], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive offsets of the keys
+      int carry = 0;
+      for (int k0 = 0; k0 <= a.b_prev; k0 += 64) {
+        const int k = k0 + lane;
+        const int x = wave_scan(k <= a.b_prev ? s_cnt[k] : 0);
+        if (k <= a.b_prev) s_cnt[k] = carry + x;
+        carry += __shfl(x, 63, 64);
+      }
+    }
+    __syncthreads();
+    for (int b = tid; b < n; b += nt) s_perm[atomicAdd(&s_cnt[s_key[b]], 1)] = b;
+    __syncthreads();
+    for (int pos = tid; pos < n; pos += nt) rank[(size_t)r * a.B_max + s_perm[pos]] = pos;
+  } else {
+    for (int b = tid; b < n; b += nt) rank[(size_t)r * a.B_max + b] = b;
+  }
+  // one wavefront per tile: chain rows, distinct records, plan
+  for (int tile = wave; tile < ntile; tile += nwaves) {
+    const int b0 = tile * NB, nb = min(NB, n - b0);
+    const bool live = lane < nb;
+    const int pos = b0 + min(lane, nb - 1);
+    const int b = sorted ? s_perm[pos] : pos;
+    const int p = sorted ? s_par[b] : parent_of(b);
+    const int32_t* prow = a.chain_prev + ((size_t)r * a.B_max + p) * L;
+    int32_t* out = a.chain_out + ((size_t)r * a.B_max + b) * L;
+    unsigned char* rec = plan + ((size_t)r * ntile + tile) * plan_bytes;
+    int* dlist = reinterpret_cast<int*>(rec + 4);
+    unsigned char* li = rec + li_off;
+    int base = 0;
+    for (int m = 0; m < L; ++m) {
+      if (m >= nch) {  // own slot, then -1
+        if (live) out[m] = m == nch ? nch * a.B_max + b : -1;
+        continue;
+      }
+      const int v = prow[m];
+      if (live) out[m] = v;
+      // the first beam of the tile with the same record at this position (records at different positions
+      // differ: position m holds slots of step m + 1)
+      int o = lane;
+      for (int c = nb - 1; c >= 0; --c)
+        if (__builtin_amdgcn_readlane(v, c) == v) o = c;
+      const unsigned long long first = __ballot(live && o == lane);
+      const int place = base + __popcll(first & ((1ull << o) - 1ull));
+      if (live && o == lane && place < kCap) dlist[place] = v;
+      if (live) li[lane * L + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
+      base += __popcll(first);
+    }
+    if (lane == 0) *reinterpret_cast<int*>(rec) = base;
+    if (lane < NB) reinterpret_cast<int*>(rec + perm_off)[lane] = b;
+  }
+  for (int idx = tid; idx < (a.B_max - n) * L; idx += nt)  // rows of beams >= n are all -1
+    a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
+}
 
-    // ---- after the chain tables: every remaining global load is a gather whose address comes from LDS.  The
-    // gathers run as software pipelines of unconditional loads (indices past the end are clamped to a valid
-    // record and their values dropped), so that the compiler's in-order vmcnt waits cover exactly the load
-    // being consumed and never the ones issued after it.
+// ---------------------------------------------------------------------------------------------------------
+template <int NB, int RB>
+__global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs a, const unsigned char* __restrict__ plan,
+                                                                      int plan_bytes, int perm_off, int li_off,
+                                                                      Sched S) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int NW = RB / 16;      // wavefronts: wavefront w owns rows 16 w .. 16 w + 15 of the row block
+  constexpr int NT = NW * 64;
+  constexpr int VP = RB / 8;       // 16-byte pieces of a v row block (bf16)
+  constexpr int UP = RB / 4;       // 16-byte pieces of a u row block (float32)
+  constexpr int KI = (kCap * 16 + NT - 1) / NT;  // key pieces of the distinct records per thread
+  constexpr int UI = (kCap * UP + NT - 1) / NT;  // u pieces per thread
+  constexpr int NX = 2 * NB * 16 + NB * VP;      // k, q and v pieces of a tile
+  constexpr int XI = (NX + NT - 1) / NT;         // ... per thread
+  constexpr int kTiles = NB / 16;
+  const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v, t = a.t, nch = t - 1;
+  const FusedLds lay = fused_layout(NB, L, RB);
+  const int LS = coef_stride(L);
+  constexpr int ngroups = NT / 16;
+  const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs (elements)
+  unsigned char* xk = lds + lay.xk;
+  unsigned char* xq = lds + lay.xq;
+  unsigned char* xv = lds + lay.xv;
+  float* al_t = reinterpret_cast<float*>(lds + lay.al);
+  float* be_t = reinterpret_cast<float*>(lds + lay.be);
+  int* pm_t = reinterpret_cast<int*>(lds + lay.pm);
+  const unsigned char* li_t = lds + lay.li;
+  unsigned char* kd = lds + lay.kd;
+  unsigned char* ud = lds + lay.ud;
+  const float* ad = reinterpret_cast<const float*>(lds + lay.ad);
+  f32x2_t* coef = reinterpret_cast<f32x2_t*>(lds + lay.coef);
+  float* beamA = reinterpret_cast<float*>(lds + lay.beamA);
+  float* beamKq = reinterpret_cast<float*>(lds + lay.beamKq);
+
+  // What this thread needs from a tile's plan to issue the tile's loads: nd, the distinct slots of its
+  // copies into LDS, and the beams of its k, q, v pieces and of its alpha and beta.  Loaded one tile ahead.
+  struct Plan {
+    int nd, as, ab, ks[KI], us[UI], xb[XI];
+  };
+  auto piece_row = [&](int q) {  // the row (place in the tile) of k, q or v piece q
+    return q < 2 * NB * 16 ? ((q & (NB * 16 - 1)) >> 4) : (q - 2 * NB * 16) / VP;
+  };
+  auto load_plan = [&](const Cursor& c, int tid) {
+    Plan p;
+    const int tile = c.valid ? c.tile : 0;
+    const unsigned char* rec = plan + ((size_t)(c.valid ? c.J.rh / H : 0) * S.ntile + tile) * plan_bytes;
+    const int* dl = reinterpret_cast<const int*>(rec + 4);
+    const int* pm = reinterpret_cast<const int*>(rec + perm_off);
+    p.nd = *reinterpret_cast<const int*>(rec);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) p.ks[i] = dl[min((i * NT + tid) >> 4, kCap - 1)];
+#pragma unroll
+    for (int i = 0; i < UI; ++i) p.us[i] = dl[min((i * NT + tid) / UP, kCap - 1)];
+    p.as = dl[min(tid, kCap - 1)];
+    p.ab = pm[min(tid, NB - 1)];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) p.xb[i] = pm[piece_row(min(i * NT + tid, NX - 1))];
+    if (nch == 0) {  // step 1 has no plan: the beams keep their order
+      const int nb = min(NB, n - tile * NB);
+      p.nd = 0;
+      p.ab = tile * NB + min(tid, nb - 1);
+#pragma unroll
+      for (int i = 0; i < XI; ++i) p.xb[i] = tile * NB + min(piece_row(min(i * NT + tid, NX - 1)), nb - 1);
+    }
+    return p;
+  };
+  bf16x8_t sf[kKS][2];
+  int cur_job = -1;
+  Plan pl = load_plan(cursor_first(S), (int)threadIdx.x);
+  __builtin_amdgcn_s_waitcnt(0);  // so that no wait for the plan is left inside the loop
+  for (Cursor c = cursor_first(S); c.valid; c = cursor_next(S, c)) {
+    // the thread index is laundered per tile, so that the compiler derives per-lane addresses next to their
+    // use instead of keeping them live (and spilled) across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int gq = lane >> 4, col = lane & 15;
     const int g16 = tid >> 4, j16 = tid & 15;
-    const int ngroups = nthreads >> 4;
-    auto rest = [&](auto rm_c) {
-      constexpr int RM = decltype(rm_c)::value;  // chain records per tile in flight in the u ring (0: no chain)
-      constexpr int NU = RM > 0 ? RM * kTiles : 1;
-      int bcs[kTiles];  // this lane's beam in each 16-beam tile, clamped to the tile's last beam
+    const int rh = c.J.rh, r = rh / H, h = rh - r * H, rb = c.J.rb;
+    const int b0 = c.tile * NB, nb = min(NB, n - b0);
+    const size_t arena = (size_t)rh * a.slots;
+    const size_t rrow = (size_t)r * n * H + h;  // input row of beam 0 of this request at this head
+    const float* u_rd = a.rec_u + arena * d_v;  // u arena of this (request, head): [slots][d_v]
+    const unsigned char* prec = plan + ((size_t)r * S.ntile + c.tile) * plan_bytes;
+    // ---- the distinct records' keys, u rows and alphas, the beams and the plan places, copied into LDS ----
+    const bool fast = nch > 0 && pl.nd <= kCap;
+    const int ndl = fast ? pl.nd : 0;  // records copied into LDS
+    {
+      const uint16_t* kr = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
 #pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) bcs[mt] = min(mt * 16 + col, nb - 1);
-      auto u_load = [&](int mt, int m) -> f32x4_t {
-        const unsigned uo = u_index((unsigned)slot_tab[bcs[mt] * LS + m], (unsigned)dv0, (unsigned)d_v);
-        return *reinterpret_cast<const f32x4_t*>(u_rd + uo);
-      };
-      // u ring, records-major: U[r * kTiles + mt] holds record m0 + r of tile mt.  Its first RM records go out
-      // now and land during phase 1.
-      f32x4_t U[NU];
-      if constexpr (RM > 0) {
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-#pragma unroll
-          for (int mt = 0; mt < kTiles; ++mt) U[r * kTiles + mt] = u_load(mt, min(r, nch - 1));
+      for (int i = 0; i < KI; ++i) {
+        const int q0 = i * NT + wave * 64, q = q0 + lane;
+        if (q < ndl * 16) dma16(kr + (size_t)pl.ks[i] * kDK + (q & 15) * 8, kd + q0 * 16);
       }
-
-      // ---- phase 1: 16 lanes per (beam, chain record): K_j . k and K_j . q into the coefficient table.  Group g
-      // takes items g, g + ngroups, ...; a ring of kD1 chain keys per lane. ----
-      if constexpr (RM > 0) {
-        const int items = nb * nch;
-        const int kmax = (items + ngroups - 1) / ngroups;
-        u32x4_t K[kD1];
-        int IY[kD1];
-        auto k_load = [&](int kk, int d) {
-          const int2 e = item_tab[min(kk * ngroups + g16, items - 1)];
-          IY[d] = e.y;
-          K[d] = *reinterpret_cast<const u32x4_t*>(k_rd + ((unsigned)e.x * kDK + j16 * 8));
-        };
-        auto k_use = [&](int kk, int d) {
-          if (kk * ngroups + g16 < items) {  // uniform over the 16 lanes of the group
-            const int pos = IY[d] & 0xFFFF, bb = IY[d] >> 16;
-            const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
-            const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
-            const float dk = row16_sum(dot8_bf16(K[d], kx));
-            const float dq = row16_sum(dot8_bf16(K[d], qx));
-            if (j16 == 0) {
-              const float c = c_tab[pos];
-              coef[pos] = (f32x2_t){c * dk, c * dq};
+#pragma unroll
+      for (int i = 0; i < UI; ++i) {
+        // u piece p of distinct record d holds row chunk p ^ (d % UP) of the row block
+        const int q0 = i * NT + wave * 64, q = q0 + lane;
+        const int d = q / UP, ch = (q % UP) ^ (d & (UP - 1));
+        if (q < ndl * UP) dma16(u_rd + (size_t)pl.us[i] * d_v + rb * RB + 4 * ch, ud + q0 * 16);
+      }
+      if (wave == 0 && lane < ndl) dma4(a.rec_alpha + arena + pl.as, lds + lay.ad);
+      if (nch > 0) {
+        if (wave == 0 && lane < NB) dma4(prec + perm_off + lane * 4, lds + lay.pm);
+        for (int q0 = wave * 64; q0 < NB * L / 4; q0 += NT)
+          if (q0 + lane < NB * L / 4 && ndl > 0) dma4(prec + li_off + (q0 + lane) * 4, lds + lay.li + q0 * 4);
+      }
+    }
+    // ---- the k, q and v rows; alpha and beta ----
+    const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rrow * kDK;
+    const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rrow * kDK;
+    const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rrow * d_v + rb * RB;
+    u32x4_t X[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      // pieces 0 .. NB*16-1: k rows, then q rows, then v rows; a row's piece p holds chunk p ^ (row % 16)
+      const int q = min(i * NT + tid, NX - 1);
+      const int row = piece_row(q);
+      const unsigned beam = (unsigned)pl.xb[i];
+      const unsigned offk = beam * hk + (((q & 15) ^ (row & 15)) << 3);
+      const int qv = max(q - 2 * NB * 16, 0);
+      const unsigned offv = beam * hv + (((qv % VP) ^ (row & (VP - 1))) << 3);
+      const uint16_t* base = q < NB * 16 ? kin : (q < 2 * NB * 16 ? qin : vin);
+      X[i] = *reinterpret_cast<const u32x4_t*>(base + (q < 2 * NB * 16 ? offk : offv));
+    }
+    const float pal = a.alpha[rrow + (size_t)pl.ab * H];
+    const float pbe = a.beta[rrow + (size_t)pl.ab * H];
+    const int pab = pl.ab;
+    pl = load_plan(cursor_next(S, c), tid);  // the next tile's plan, in flight with this tile's loads
+    if (c.job != cur_job) {  // S_ctx rows of this wavefront, once per job
+      cur_job = c.job;
+      const int W = d_v / 32;
+      const size_t half = (size_t)W * kKS * 2 * 64;
+      const u32x4_t* fr = reinterpret_cast<const u32x4_t*>(a.sctx_frag) + (size_t)rh * 2 * half;
+      const int x = rb * NW + wave;  // 16-row block of d_v
+#pragma unroll
+      for (int k2 = 0; k2 < kKS; ++k2)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+          sf[k2][hl] = __builtin_bit_cast(bf16x8_t, fr[hl * half + (((size_t)(x >> 1) * kKS + k2) * 2 + (x & 1)) * 64 + lane]);
+    }
+    // ---- into LDS ----
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int q = i * NT + tid;
+      if (q < NX) *reinterpret_cast<u32x4_t*>(xk + q * 16) = X[i];  // the k, q and v regions are adjacent
+    }
+    if (tid < NB) {
+      al_t[tid] = pal;
+      be_t[tid] = pbe;
+      if (nch == 0) pm_t[tid] = pab;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's copies into LDS have landed
+    __syncthreads();
+    // ---- per beam (16 lanes): k . q, the chain coefficients newest to oldest, the record key and alpha ----
+    for (int b = g16; b < nb; b += ngroups) {
+      const int beam = pm_t[b];
+      const int xo = b * kRow + ((j16 ^ (b & 15)) << 4);
+      const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xk + xo);
+      const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xq + xo);
+      const float kq = row16_sum(dot8_bf16(kx, qx));
+      float cdec = 1.f;
+      if (fast) {
+        // four chain records at a time: their LDS reads and dot products are independent; the decay product is
+        // then applied newest to oldest
+        for (int m = nch - 1; m >= 0; m -= 4) {
+          int d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d[j] = li_t[b * L + max(m - j, 0)];
+          u32x4_t K[4];
+          float am[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            K[j] = *reinterpret_cast<const u32x4_t*>(kd + d[j] * kRow + j16 * 16);
+            am[j] = ad[d[j]];
+          }
+          float dk[4], dq[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dk[j] = row16_sum(dot8_bf16(K[j], kx));
+            dq[j] = row16_sum(dot8_bf16(K[j], qx));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (m - j >= 0) {
+              if (j16 == 0) coef[b * LS + m - j] = (f32x2_t){cdec * dk[j], cdec * dq[j]};
+              cdec *= am[j];
             }
-          }
-        };
-#pragma unroll
-        for (int d = 0; d < kD1; ++d) k_load(d, d);
-        int k0 = 0;
-        for (; k0 + kD1 < kmax; k0 += kD1) {
-#pragma unroll
-          for (int d = 0; d < kD1; ++d) {
-            k_use(k0 + d, d);
-            k_load(k0 + kD1 + d, d);
-          }
         }
-#pragma unroll
-        for (int d = 0; d < kD1; ++d) k_use(k0 + d, d);
-      }
-      // k . q of every beam; append the record key and alpha
-      for (int bb = g16; bb < nb; bb += ngroups) {
-        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + j16 * 16);
-        const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + j16 * 16);
-        const float kq = row16_sum(dot8_bf16(kx, qx));
-        const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-        *reinterpret_cast<u32x4_t*>(k_wr + (own * kDK + j16 * 8)) = kx;
-        if (j16 == 0) {
-          beamKq[bb] = kq;
-          al_wr[own] = beamAl[bb];
+      } else {
+        const int32_t* crow = a.chain_out + ((size_t)r * a.B_max + beam) * L;
+        for (int m = nch - 1; m >= 0; --m) {
+          const int sl = crow[m];
+          const u32x4_t K = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.rec_k) + (arena + sl) * kDK + j16 * 8);
+          const float am = a.rec_alpha[arena + sl];
+          const float dk = row16_sum(dot8_bf16(K, kx));
+          const float dq = row16_sum(dot8_bf16(K, qx));
+          if (j16 == 0) coef[b * LS + m] = (f32x2_t){cdec * dk, cdec * dq};
+          cdec *= am;
         }
       }
-      __syncthreads();
-
-      // ---- phase 2: the replay over the u ring (sums per tile in P, Q), then per tile the MFMA contraction,
-      // u and o ----
-      floatx4_t P[kTiles], Q[kTiles];
-#pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) {
-        P[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-        Q[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      if (j16 == 0) {
+        beamA[b] = cdec;
+        beamKq[b] = kq;
       }
-      if constexpr (RM > 0) {
-        auto acc = [&](int mt, int m, int i) {
-          if (mt * 16 < nb) {
-            const f32x2_t c = coef[bcs[mt] * LS + m];
+      if (rb == 0) {  // the new record's key and alpha
+        const unsigned own = (unsigned)(nch * a.B_max + beam);
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.rec_k) + (arena + own) * kDK + j16 * 8) = kx;
+        if (j16 == 0) a.rec_alpha[arena + own] = al_t[b];
+      }
+    }
+    if (nch == 0 && h == 0 && rb == 0) {  // step 1: the first chain rows, and the parents must all be 0
+      for (int b = tid; b < nb; b += NT) {
+        if (a.parent[(size_t)r * n + b0 + b] != 0) *a.flag = a.epoch;
+        int32_t* row = a.chain_out + ((size_t)r * a.B_max + b0 + b) * L;
+        row[0] = b0 + b;
+        for (int m = 1; m < L; ++m) row[m] = -1;
+      }
+      if (c.tile == S.ntile - 1)
+        for (int idx = tid; idx < (a.B_max - n) * L; idx += NT) a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
+    }
+    __syncthreads();  // coefficient table ready
+    // ---- per 16-beam tile: S_ctx contraction, replay, new record u, output ----
+    const int dvl = wave * 16 + 4 * gq;  // this lane's rows within the row block: dvl .. dvl + 3
+    const int dv0 = rb * RB + dvl;
+    float* u_wr = a.rec_u + arena * d_v;
+#pragma unroll
+    for (int mt = 0; mt < kTiles; ++mt) {
+      if (mt * 16 >= nb) break;
+      const int bb = mt * 16 + col;
+      const int bc = min(bb, nb - 1);
+      floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k2 = 0; k2 < kKS; ++k2) {
+        const int off = bb * kRow + (((k2 * 4 + gq) ^ (bb & 15)) << 4);
+        const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xk + off));
+        const bf16x8_t bq = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xq + off));
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+          pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[k2][hl], bk, pk, 0, 0, 0);
+          pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[k2][hl], bq, pq, 0, 0, 0);
+        }
+      }
+      floatx4_t P = (floatx4_t){0.f, 0.f, 0.f, 0.f}, Q = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      if (fast) {
+        // four chain records at a time, their LDS reads issued together
+        for (int m0 = 0; m0 < nch; m0 += 4) {
+          int d[4];
+          f32x2_t cf[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int mm = min(m0 + j, nch - 1);
+            d[j] = li_t[bc * L + mm];
+            cf[j] = coef[bc * LS + mm];
+            if (m0 + j >= nch) cf[j] = (f32x2_t){0.f, 0.f};
+          }
+          f32x4_t uu[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            uu[j] = *reinterpret_cast<const f32x4_t*>(ud + d[j] * (RB * 4) + (((dvl >> 2) ^ (d[j] & (UP - 1))) << 4));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              P[mt][e] += c.x * U[i][e];
-              Q[mt][e] += c.y * U[i][e];
-            }
-          }
-        };
-        int m0 = 0;
-        for (; m0 + RM < nch; m0 += RM) {
-#pragma unroll
-          for (int r = 0; r < RM; ++r)
-#pragma unroll
-            for (int mt = 0; mt < kTiles; ++mt) {
-              acc(mt, m0 + r, r * kTiles + mt);
-              U[r * kTiles + mt] = u_load(mt, min(m0 + RM + r, nch - 1));
+              P[e] += cf[j].x * uu[j][e];
+              Q[e] += cf[j].y * uu[j][e];
             }
         }
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-          if (m0 + r < nch) {
-#pragma unroll
-            for (int mt = 0; mt < kTiles; ++mt) acc(mt, m0 + r, r * kTiles + mt);
-          }
-      }
-#pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) {
-        if (mt * 16 >= nb) break;
-        const int bb = mt * 16 + col;
-        floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-        // B operand: lane l holds column (beam) l % 16, k = 8 (l / 16) .. +7 of this k-step
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          const bf16x8_t bk = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kXRow + ks * 64 + gq * 16));
-          const bf16x8_t bq = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (NB + bb) * kXRow + ks * 64 + gq * 16));
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl) {
-            pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bk, pk, 0, 0, 0);
-            pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks][hl], bq, pq, 0, 0, 0);
-          }
-        }
-        if (bb < nb) {
-          const float A = beamA[bb], al = beamAl[bb], be = beamBe[bb], kq = beamKq[bb];
-          const unsigned own = (unsigned)(nch * a.B_max + b0 + bb);
-          const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(vs + bb * lay.vrow + dv0 * 2);
-          const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
-          const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16),
-                               bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16)};
-          f32x4_t u4, o4;
+      } else {
+        const int32_t* crow = a.chain_out + ((size_t)r * a.B_max + pm_t[bc]) * L;
+        for (int m = 0; m < nch; ++m) {
+          const f32x2_t cf = coef[bc * LS + m];
+          const f32x4_t uu = *reinterpret_cast<const f32x4_t*>(u_rd + (size_t)crow[m] * d_v + dv0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float uu = be * (v4[e] - al * (A * pk[e] + P[mt][e]));
-            u4[e] = uu;
-            o4[e] = al * (A * pq[e] + Q[mt][e]) + kq * uu;
+            P[e] += cf.x * uu[e];
+            Q[e] += cf.y * uu[e];
           }
-          *reinterpret_cast<f32x4_t*>(u_wr + u_index(own, (unsigned)dv0, (unsigned)d_v)) = u4;  // 1 KB per wave
-          *reinterpret_cast<f32x4_t*>(o_wr + ((unsigned)bb * hv + dv0)) = o4;
         }
       }
-    };
-    if (nch == 0)
-      rest(IntC<0>{});
-    else if (nch == 1)
-      rest(IntC<1>{});
-    else
-      rest(IntC<(NB >= 128 ? 1 : kRM)>{});  // 8 tiles per lane: one record per tile in flight
-  };
-
-  if constexpr (PERSIST) {
-    load_sf((int)threadIdx.x >> 6, (int)threadIdx.x & 63);
-    const int tile_end = min(ntile, (split + 1) * tps);
-    for (int tile = split * tps; tile < tile_end; ++tile) {
-      // the thread index is laundered per tile, so that the compiler derives the per-lane addresses next to
-      // their use instead of keeping them live (and spilled) across the loop
-      int tid = threadIdx.x;
-      asm volatile("" : "+v"(tid));
-      do_tile(tile, tid);
-      if (tile + 1 < tile_end) __syncthreads();  // the next tile overwrites the LDS tables
+      if (bb < nb) {
+        const int beam = pm_t[bb];
+        const float A = beamA[bb], kq = beamKq[bb];
+        const float al = al_t[bb], be = be_t[bb];
+        const int vc = dvl >> 3;  // 16-byte piece of the v row block
+        const f32x2_t vv = *reinterpret_cast<const f32x2_t*>(xv + bb * RB * 2 + ((vc ^ (bb & (VP - 1))) << 4) + (gq & 1) * 8);
+        const uint32_t w0 = __float_as_uint(vv.x), w1 = __float_as_uint(vv.y);
+        const float v4[4] = {bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16), bf16_bits_to_f32(w1 & 0xFFFFu),
+                             bf16_bits_to_f32(w1 >> 16)};
+        f32x4_t u4, o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float uu = be * (v4[e] - al * (A * pk[e] + P[e]));
+          u4[e] = uu;
+          o4[e] = al * (A * pq[e] + Q[e]) + kq * uu;
+        }
+        const unsigned own = (unsigned)(nch * a.B_max + beam);
+        *reinterpret_cast<f32x4_t*>(u_wr + (size_t)own * d_v + dv0) = u4;
+        *reinterpret_cast<f32x4_t*>(a.o + (rrow + (size_t)beam * H) * d_v + dv0) = o4;
+      }
     }
-  } else {
-    do_tile(split, (int)threadIdx.x);
+    __syncthreads();  // the next tile overwrites the LDS
   }
 }
 
+// ---------------------------------------------------------------------------------------------------------
 bool fused_supported(int d_k, int d_v, int L_max) {
-  return d_k == kDK && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && fused_lds_bytes(16, L_max, d_v) <= 160 * 1024;
+  return d_k == kDK && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && L_max <= 64 &&
+         fused_lds_bytes(16, L_max, d_v) <= 160 * 1024;
 }
 
 size_t fused_lds_bytes(int tile, int L_max, int d_v) {
-  return (size_t)fused_layout(tile, L_max, d_v).total;
+  return (size_t)fused_layout(tile, L_max, row_block(d_v)).total;
 }
 
-int fused_pick_tile(int R, int H, int n, int d_v, int L_max, int requested) {
+int fused_pick_tile(int d_v, int L_max, int requested) {
   if (requested) return requested;
-  const long G = (long)R * H;
-  const int cands[3] = {64, 32, 16};
-  for (int c : cands) {
-    const long wgs = G * ((n + c - 1) / c);
-    if (wgs >= 1024 && fused_lds_bytes(c, L_max, d_v) <= lds_budget(d_v)) return c;
-  }
-  return 16;
+  return fused_lds_bytes(32, L_max, d_v) <= 80 * 1024 ? 32 : 16;
 }
 
 namespace {
-using FusedKernel = void (*)(StepArgs, int, int);
-hipError_t launch_fused_as(FusedKernel k, dim3 grid, dim3 block, size_t lds, hipStream_t s, const StepArgs& a,
-                           int ntile, int tps) {
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k, grid, block, lds, s, a, ntile, tps);
-  return hipGetLastError();
+// Bytes of the largest plan area of a configuration (either tile size); the processing order follows it.
+size_t plan_area_bytes(int R, int B_max, int L_max) {
+  size_t most = 0;
+  for (int nb : {16, 32}) most = std::max(most, (size_t)R * ((B_max + nb - 1) / nb) * plan_layout(nb, L_max).bytes);
+  return (most + 255) & ~(size_t)255;
 }
 }  // namespace
 
-hipError_t launch_step_fused(const StepArgs& a, int tile, hipStream_t s) {
-  const int ntile = (a.n + tile - 1) / tile;
-  // A workgroup has d_v / 16 waves of up to 128 VGPRs: the register file admits 16 / (d_v / 16) per CU.  When
-  // it admits one, each workgroup runs kPersistTiles consecutive tiles of its (request, head): no CU then idles
-  // between one workgroup's last store and the next one's launch, and S_ctx is read once per run.
-  const bool persist = 16 / (a.d_v / 16) < 2;
-  const int tps = persist ? std::min(ntile, kPersistTiles) : 1;
-  const int nsplit = (ntile + tps - 1) / tps;
-  dim3 grid((unsigned)((size_t)a.R * a.H * nsplit)), block(4 * a.d_v);
-  const size_t lds = fused_lds_bytes(tile, a.L_max, a.d_v);
-#define ONELA_FUSED_CASE(NB)                                                                     \
-  case NB:                                                                                       \
-    return persist ? launch_fused_as(&step_fused_kernel<NB, true>, grid, block, lds, s, a, ntile, tps) \
-                   : launch_fused_as(&step_fused_kernel<NB, false>, grid, block, lds, s, a, ntile, tps);
-  switch (tile) {
-    ONELA_FUSED_CASE(16)
-    ONELA_FUSED_CASE(32)
-    ONELA_FUSED_CASE(64)
-    ONELA_FUSED_CASE(128)
-    default:
-      return hipErrorInvalidValue;
+size_t fused_plan_bytes(int R, int B_max, int L_max) {
+  return plan_area_bytes(R, B_max, L_max) + (size_t)R * B_max * 4;  // plans, then rank[R][B_max]
+}
+
+namespace {
+using FusedKernel = void (*)(StepArgs, const unsigned char*, int, int, int, Sched);
+FusedKernel fused_kernel_for(int tile, int rb) {
+#define ONELA_FUSED_RB(NB)                              \
+  switch (rb) {                                         \
+    case 32: return &step_fused_kernel<NB, 32>;         \
+    case 64: return &step_fused_kernel<NB, 64>;         \
+    case 128: return &step_fused_kernel<NB, 128>;       \
+    default: return nullptr;                            \
   }
-#undef ONELA_FUSED_CASE
+  if (tile == 16) { ONELA_FUSED_RB(16) }
+  if (tile == 32) { ONELA_FUSED_RB(32) }
+#undef ONELA_FUSED_RB
+  return nullptr;
+}
+}  // namespace
+
+hipError_t fused_prepare(int tile, int d_v, int L_max, int* grid) {
+  const int rb = row_block(d_v);
+  FusedKernel k = fused_kernel_for(tile, rb);
+  if (!k) return hipErrorInvalidValue;
+  const size_t lds = fused_lds_bytes(tile, L_max, d_v);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  const int threads = 64 * (rb / 16);
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), threads, lds)) !=
+      hipSuccess)
+    return e;
+  *grid = std::max(1, cus * std::max(per_cu, 1));
+  return hipSuccess;
+}
+
+hipError_t launch_step_fused(const StepArgs& a, int tile, void* plan, int grid, hipStream_t s) {
+  const int rb = row_block(a.d_v);
+  FusedKernel k = fused_kernel_for(tile, rb);
+  if (!k) return hipErrorInvalidValue;
+  const PlanLayout pl = plan_layout(tile, a.L_max);
+  const int ntile = (a.n + tile - 1) / tile;
+  unsigned char* pb = static_cast<unsigned char*>(plan);
+  int* rank = reinterpret_cast<int*>(pb + plan_area_bytes(a.R, a.B_max, a.L_max));
+  if (a.t > 1) {
+    if (tile == 16)
+      hipLaunchKernelGGL(ancestry_plan_kernel<16>, dim3((unsigned)a.R), dim3(1024), 0, s, a, pb, pl.bytes, pl.perm,
+                         pl.li, rank);
+    else
+      hipLaunchKernelGGL(ancestry_plan_kernel<32>, dim3((unsigned)a.R), dim3(1024), 0, s, a, pb, pl.bytes, pl.perm,
+                         pl.li, rank);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const Sched S = make_sched(a.R * a.H, a.d_v / rb, ntile, grid);
+  const int g = std::min(grid, S.njobs);
+  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(64 * (rb / 16)), fused_lds_bytes(tile, a.L_max, a.d_v), s, a, pb,
+                     pl.bytes, pl.perm, pl.li, S);
+  return hipGetLastError();
 }
 
 }  // namespace onela

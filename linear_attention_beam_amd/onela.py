@@ -193,18 +193,6 @@ def beam_select(beam_scores, logp, n_beams: int, scratch=None):
     return parent, token, scores
 
 
-def pad16(x: int) -> int:
-    return (x + 15) // 16 * 16
-
-
-def unblock_u(blocks, slots: int, d_v: int):
-    """Record u arena [R, H, S16 * D16] in 16 x 16 tiles (see onela_view.rec_u) -> a [R, H, slots, d_v] copy."""
-    R, H = blocks.shape[0], blocks.shape[1]
-    S16, D16 = pad16(slots), pad16(d_v)
-    t = blocks.reshape(R, H, S16 // 16, D16 // 16, 16, 16).permute(0, 1, 2, 4, 3, 5)
-    return t.reshape(R, H, S16, D16)[:, :, :slots, :d_v].contiguous()
-
-
 class OneLA:
     """A decode context on one GPU: R requests x H heads, up to max_beams beams and max_steps steps.
 
@@ -293,8 +281,7 @@ class OneLA:
             return onela_get_status(self.handle, self._stream())
 
     def view(self) -> dict:
-        """Torch views of the decode state inside the workspace (read-only by convention); rec_u is
-        [R, H, slots, d_v] (an untiled copy when the fused kernel keeps it in tiles)."""
+        """Torch views of the decode state inside the workspace (read-only by convention)."""
         torch = self._torch
         v = onela_get_view(self.handle)
         c = self.cfg
@@ -312,10 +299,7 @@ class OneLA:
         return {
             "t": v.t, "n_beams": v.n_beams, "slots": slots, "fused": bool(v.fused),
             "rec_k": sub(v.rec_k, R * H * slots * dk, self.qkv_torch_dtype, (R, H, slots, dk)),
-            "rec_u": None if not v.rec_u else (
-                unblock_u(sub(v.rec_u, R * H * pad16(slots) * pad16(dv), torch.float32,
-                              (R, H, pad16(slots) * pad16(dv))), slots, dv) if v.fused
-                else sub(v.rec_u, R * H * slots * dv, torch.float32, (R, H, slots, dv))),
+            "rec_u": sub(v.rec_u, R * H * slots * dv, torch.float32, (R, H, slots, dv)),
             "rec_alpha": sub(v.rec_alpha, R * H * slots, torch.float32, (R, H, slots)),
             "chains": sub(v.chains, L * R * B * L, torch.int32, (L, R, B, L)),
             "sctx_t": sub(v.sctx_t, R * H * dk * dv, torch.float32, (R, H, dk, dv)),

@@ -45,11 +45,14 @@ def expected_bytes(c):
     fused = (c.mode == onela.ONELA_MODE_REPLAY and c.qkv_dtype == onela.ONELA_BF16 and not c.flags
              and dk == 128 and dv % 32 == 0)
     total = 256 + up(R * H * dk * dv * 4) + up(R * H * dk * dv * 4 if fused else 0) + up(L * R * B * L * 4)
-    total += up(2 * R * H * B * (L + 1) * 4 if fused else 0)
+    a16 = lambda x: (x + 15) // 16 * 16  # noqa: E731
+    # per (request, tile of 16 or 32 beams) plans: nd and up to 64 distinct slots, the tile's beams, one byte per
+    # (beam, chain position); the larger of the two tile sizes, then the processing order rank[R][B]
+    plan = up(max(R * (-(-B // nb)) * (a16(4 + 4 * 64) + 4 * nb + a16(nb * L)) for nb in (16, 32))) + R * B * 4
+    total += up(plan if fused else 0)
     if c.mode == onela.ONELA_MODE_REPLAY:
         slots = B * L
-        pad16 = lambda x: (x + 15) // 16 * 16  # noqa: E731  (u records: 16 x 16 blocks of slots x rows)
-        u_elems = pad16(slots) * pad16(dv) if fused else slots * dv
+        u_elems = slots * dv
         total += up(R * H * slots * dk * s_in) + up(R * H * u_elems * 4) + up(R * H * slots * 4)
     else:
         total += up(2 * R * H * B * dk * dv * 4)
@@ -68,7 +71,7 @@ def test_workspace_size(kw):
 
 @pytest.mark.parametrize("kw", [
     dict(num_requests=0), dict(num_heads=-1), dict(d_k=0), dict(d_v=257), dict(max_beams=0),
-    dict(max_steps=0), dict(max_steps=65), dict(qkv_dtype=7), dict(mode=2), dict(flags=4), dict(tile_beams=48),
+    dict(max_steps=0), dict(max_steps=65), dict(qkv_dtype=7), dict(mode=2), dict(flags=4), dict(tile_beams=48), dict(tile_beams=64),
 ])
 def test_bad_config_is_rejected(kw):
     with pytest.raises(onela.OnelaError) as e:
@@ -101,17 +104,3 @@ def test_beam_select_bad_args(args, status):
     with pytest.raises(onela.OnelaError) as e:
         onela.onela_beam_select_scratch(*args)
     assert e.value.status == status
-
-
-@pytest.mark.parametrize("slots,d_v", [(32, 128), (20, 7), (1, 1), (48, 256)])
-def test_u_record_tiling(slots, d_v):
-    """The binding's untiling of the u arena follows the tile formula documented for onela_view.rec_u."""
-    import torch
-    S16, D16 = onela.pad16(slots), onela.pad16(d_v)
-    flat = torch.full((2, 3, S16 * D16), -1.0, dtype=torch.float64)
-    for s in range(slots):
-        for i in range(d_v):
-            flat[:, :, ((s // 16) * (D16 // 16) + i // 16) * 256 + (s % 16) * 16 + i % 16] = s * 1000 + i
-    got = onela.unblock_u(flat, slots, d_v)
-    want = torch.arange(slots, dtype=torch.float64)[:, None] * 1000 + torch.arange(d_v, dtype=torch.float64)
-    assert torch.equal(got, want.expand(2, 3, slots, d_v))

@@ -48,8 +48,8 @@ RAGGED = [1, 37, 100, 64, 99]
 
 
 @pytest.mark.parametrize("d_v,tile,generic", [
-    (128, 16, False), (128, 32, False), (128, 64, False), (128, 128, False), (64, 0, False), (256, 0, False),
-    (32, 128, False), (96, 32, False), (128, 0, True),
+    (128, 16, False), (128, 32, False), (256, 16, False), (256, 32, False), (64, 0, False), (256, 0, False),
+    (32, 16, False), (96, 32, False), (128, 0, True),
 ])
 def test_ragged_beams(d_v, tile, generic):
     cfg = inputs.config(2, R=3, H=5, d_v=d_v, B=100, L=len(RAGGED))
@@ -67,7 +67,7 @@ def test_ragged_beams(d_v, tile, generic):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
 
 
-@pytest.mark.parametrize("d_v,tile", [(128, 16), (96, 32), (224, 64), (32, 0)])
+@pytest.mark.parametrize("d_v,tile", [(128, 16), (96, 32), (224, 16), (32, 0)])
 def test_odd_record_capacity(d_v, tile):
     """max_beams = 37: the slots of a (request, head) are not a multiple of 16, so the fused kernel's last
     16-slot tile of u records is partial (the arena is padded); every head and record checked."""
@@ -85,11 +85,11 @@ def test_tiles_and_xcd_mapping_agree():
     cfg = inputs.config(2, R=2, H=8, B=96, L=3)
     steps = inputs.decode_inputs(cfg)
     sctx = short_prefill_sctx(cfg)
-    runs = [gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=t) for t in (16, 32, 64, 128)]
+    runs = [gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=t) for t in (16, 32)]
     for run in runs[1:]:
         for t in range(cfg.L):
             assert (run.outs[t] - runs[0].outs[t]).abs().max().item() <= 1e-6
-    gu.log(f"  max|o err|={check_all_heads(runs[2], cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+    gu.log(f"  max|o err|={check_all_heads(runs[-1], cfg, steps, sctx, cfg.B, cfg.L):.3g}")
 
 
 @pytest.mark.parametrize("generic", [False, True])

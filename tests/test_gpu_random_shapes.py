@@ -24,7 +24,7 @@ def draw_case(i):
     L = int(rng.integers(1, 10))
     B_max = int(rng.choice([1, 7, 16, 37, 64, 100, 130, 200]))
     beams = [int(rng.integers(1, B_max + 1)) for _ in range(L)]
-    tile = int(rng.choice([0, 16, 32, 64, 128]))
+    tile = int(rng.choice([0, 16, 32]))
     kernel = str(rng.choice(["fused", "fused", "fused", "generic", "materialize"]))
     small_alpha = bool(rng.random() < 1 / 3)
     return dict(R=R, H=H, d_v=d_v, L=L, B_max=B_max, beams=beams, tile=tile, kernel=kernel,
