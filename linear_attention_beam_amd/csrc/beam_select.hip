@@ -8,26 +8,36 @@
 // order-preserving unsigned integer (-0 and +0 map alike), the low word is ~f.  Keys are unique, so the
 // top set and its order are unique too.
 //
-// Selection without sorting everything: an MSB-first radix select finds, among the keys held in LDS, the
-// smallest key T such that exactly K keys are >= T (8-bit digits from the highest bit where the keys
-// differ; it stops as soon as a whole digit bucket is taken).  The keys >= T are then compacted.
-//   Reduce  workgroups of 8192 keys each keep their K best (unordered) in the caller's scratch buffer;
-//           repeated until a request has at most 8192 keys left.  The first pass builds the keys from the
-//           scores on the fly.
-//   Final   one workgroup per request selects its K keys from the survivors (or straight from the scores
-//           when there are few enough), orders them by counting ranks and writes parent, token, score.
-// Key 0 pads short chunks and ranks below every real key.
+// Selection without sorting everything: a workgroup of 1024 threads holds up to 8192 keys in registers
+// (8 per thread) and an MSB-first radix select finds the smallest key T such that exactly K keys are >= T
+// (8-bit digits from the highest bit where the keys differ, one LDS histogram per pass; it stops as soon as
+// a whole digit bucket is taken).  The keys >= T are then compacted.
+//   Chunk   each workgroup reduces 8192 keys of one request to its K best (unordered); repeated until a
+//           request has at most 8192 keys left (one launch for 32 x 512 x 256 -> 512).
+//   Finish  one workgroup selects a request's K keys from at most 8192 (chunk survivors or the scores
+//           themselves), orders them (sorted runs of 64, then ranks by binary search) and writes parent,
+//           token, score.
+// The two phases are separate launches: a single launch whose last-arriving chunk workgroup finishes the
+// request needs a device-scope release per workgroup, and on this chip each one writes back the XCD's L2;
+// measured, that costs more than the launch boundary it saves.  Key 0 pads short chunks and ranks below
+// every real key.
 #include "device_common.h"
 #include "launchers.h"
+
+// Whole-wave 64-bit unsigned min / max of the device library (the HIP headers declare them only under an
+// opt-in macro).
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_min_u64(unsigned long long);
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(unsigned long long);
 
 namespace onela {
 
 namespace {
-constexpr int kRedChunk = 8192;   // keys per reduce workgroup
-constexpr int kRedThreads = 1024;
-constexpr int kFinalMax = 8192;   // keys one final workgroup holds in LDS
-constexpr int kFinalThreads = 1024;
+constexpr int kThreads = 1024;
+constexpr int kPerThread = 8;
+constexpr int kChunk = kThreads * kPerThread;  // keys per workgroup
 constexpr int kMaxBeams = 2048;
+constexpr int kHistCopies = 8;                 // lanes l with l % 8 == c share histogram copy c
+constexpr int kHistStride = 260;               // ints per copy: the copies of one digit sit in different banks
 
 __device__ __forceinline__ uint32_t score_order(float x) {
   uint32_t u = __float_as_uint(x);
@@ -39,71 +49,106 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t f) {
   return ((uint64_t)score_order(s) << 32) | (uint64_t)(~f);
 }
 
-// LDS scratch of the radix select: 256-bin histograms (one per wave, at most 8, shared round robin), the
-// chosen digit, rank and bucket size, and the smallest and largest real key (key 0 is padding).
-template <int NT>
-struct SelShared {
-  static constexpr int kCopies = NT / 64 < 8 ? NT / 64 : 8;
-  int hist[kCopies][256];
+// LDS of one selection workgroup: the radix histograms and choices, per-wave extremes, and (finish only) the
+// K survivors and their sorted runs of 64.
+struct alignas(16) SelLds {
+  int hist[kHistCopies][kHistStride];
+  unsigned long long wmin[kThreads / 64], wmax[kThreads / 64];
   int digit, rank, count, n_out;
-  unsigned long long kmin, kmax;
+  uint64_t best[kMaxBeams];
+  uint64_t sorted[kMaxBeams];
 };
 
-// Smallest key T such that exactly K of the n unique keys in `keys` are >= T (requires 1 <= K <= the number
-// of nonzero keys).  Every thread of the workgroup must call it; NT is the workgroup size.  Digits start at
-// the highest bit where the smallest and the largest real key differ: the bits above are common to all of
-// them and would only cost passes that split nothing.
-template <int NT>
-__device__ uint64_t radix_threshold(const uint64_t* keys, int n, int K, SelShared<NT>& sh) {
-  constexpr int kCopies = SelShared<NT>::kCopies;
-  const int tid = threadIdx.x, lane = tid & 63, wv = (tid >> 6) % kCopies;
+// This thread's keys of positions [base, base + kChunk) of request r, position base + e * 1024 + tid in
+// slot e, padded with 0 past n_in.  Built from the scores (src == nullptr) or read from a key buffer.
+__device__ __forceinline__ void load_keys(uint64_t (&key)[kPerThread], const float* beam_scores,
+                                          const float* logp, const uint64_t* src, long n_in, int n_prev,
+                                          int n_cand, int r, long base) {
+  const int tid = threadIdx.x;
+  if (src == nullptr) {
+    const float* bs = beam_scores + (size_t)r * n_prev;
+    const float* lp = logp + (size_t)r * n_in;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const long i = base + e * kThreads + tid;
+      uint64_t k = 0;
+      if (i < n_in) {
+        const uint32_t f = (uint32_t)i;
+        k = make_key(bs[f / (uint32_t)n_cand] + lp[f], f);
+      }
+      key[e] = k;
+    }
+  } else {
+    const uint64_t* s = src + (size_t)r * n_in;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const long i = base + e * kThreads + tid;
+      key[e] = i < n_in ? s[i] : 0ull;
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, int off) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, off, 64), hi = __shfl_xor((uint32_t)(x >> 32), off, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Smallest key T such that exactly K of the workgroup's unique keys are >= T (requires 1 <= K <= the number
+// of nonzero keys).  Every thread must call it.  Digits start at the highest bit where the smallest and the
+// largest real key differ: the bits above are common to all of them and would only cost passes that split
+// nothing.
+__device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerThread], int K, SelLds& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, copy = lane & (kHistCopies - 1);
   unsigned long long lo = ~0ull, hi = 0ull;
-  for (int i = tid; i < n; i += NT) {
-    const unsigned long long k = keys[i];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const unsigned long long k = key[e];
     if (k != 0ull) {
       lo = k < lo ? k : lo;
       hi = k > hi ? k : hi;
     }
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned long long l2 = __shfl_xor(lo, off, 64), h2 = __shfl_xor(hi, off, 64);
-    lo = l2 < lo ? l2 : lo;
-    hi = h2 > hi ? h2 : hi;
-  }
-  if (tid == 0) {
-    sh.kmin = ~0ull;
-    sh.kmax = 0ull;
-  }
-  __syncthreads();
+  lo = __ockl_wfred_min_u64(lo);
+  hi = __ockl_wfred_max_u64(hi);
   if (lane == 0) {
-    atomicMin(&sh.kmin, lo);
-    atomicMax(&sh.kmax, hi);
+    sh.wmin[wave] = lo;
+    sh.wmax[wave] = hi;
   }
+  for (int i = tid; i < kHistCopies * kHistStride; i += kThreads) (&sh.hist[0][0])[i] = 0;
   __syncthreads();
-  const uint64_t kmax = sh.kmax, diff = kmax ^ sh.kmin;
+  lo = ~0ull;
+  hi = 0ull;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    lo = sh.wmin[w] < lo ? sh.wmin[w] : lo;
+    hi = sh.wmax[w] > hi ? sh.wmax[w] : hi;
+  }
+  const uint64_t kmax = hi, diff = hi ^ lo;
   if (diff == 0) return kmax;  // a single real key
   int top = 63 - __clzll((long long)diff);
   uint64_t mask = top == 63 ? 0ull : ~((2ull << top) - 1), prefix = kmax & mask;
   int rank = K;
-  while (top >= 0) {
+  for (;;) {
     const int w = top >= 7 ? 8 : top + 1, shift = top - w + 1;
-    for (int i = tid; i < kCopies * 256; i += NT) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint64_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&sh.hist[wv][(int)((k >> shift) & 0xFFu)], 1);
-    }
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if ((key[e] & mask) == prefix) atomicAdd(&sh.hist[copy][(int)((key[e] >> shift) & 0xFFu)], 1);
     __syncthreads();
     if (tid < 64) {
-      // lane l holds digits 255 - 4l .. 252 - 4l: lane order is descending digit order
-      int c[4], local = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int v = 0;
-        for (int x = 0; x < kCopies; ++x) v += sh.hist[x][255 - 4 * tid - e];
-        c[e] = v;
-        local += v;
+      // lane l holds digits 255 - 4l .. 252 - 4l (c[e]: digit 255 - 4l - e): lane order is descending digit
+      // order.  The copies are summed and cleared for the next pass.
+      int c[4] = {0, 0, 0, 0};
+#pragma unroll 2
+      for (int x = 0; x < kHistCopies; ++x) {
+        int4* h4 = reinterpret_cast<int4*>(&sh.hist[x][252 - 4 * tid]);
+        const int4 v = *h4;
+        *h4 = make_int4(0, 0, 0, 0);
+        c[0] += v.w;
+        c[1] += v.z;
+        c[2] += v.y;
+        c[3] += v.x;
       }
+      const int local = c[0] + c[1] + c[2] + c[3];
       int incl = local;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -125,127 +170,110 @@ __device__ uint64_t radix_threshold(const uint64_t* keys, int n, int K, SelShare
       }
     }
     __syncthreads();
+    // the next pass's histogram atomics come after this read, and the choice is rewritten only after the
+    // next pass's barrier: no barrier is needed here
     const int d = sh.digit, cnt = sh.count;
     rank = sh.rank;
     prefix |= (uint64_t)d << shift;
     mask |= (uint64_t)((1u << w) - 1u) << shift;
-    if (cnt == rank) break;  // the whole bucket is taken: exactly K keys are >= prefix
+    if (cnt == rank || shift == 0) break;  // the whole bucket is taken: exactly K keys are >= prefix
     top = shift - 1;
-    __syncthreads();         // everyone has read the choice before the next pass rewrites it
   }
   return prefix;
 }
 
-// Write the keys >= thr (K of them) to out[0 .. K) in arbitrary order.
-template <int NT>
-__device__ void compact(const uint64_t* keys, int n, uint64_t thr, uint64_t* out, SelShared<NT>& sh) {
+// Write this workgroup's keys >= thr (K of them) to out[0 .. K) in arbitrary order (out: global or LDS).
+__device__ __forceinline__ void compact(const uint64_t (&key)[kPerThread], uint64_t thr, uint64_t* out, SelLds& sh) {
   if (threadIdx.x == 0) sh.n_out = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint64_t k = keys[i];
-    const uint64_t take = __ballot(k >= thr);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool mine = key[e] >= thr;
+    const uint64_t take = __ballot(mine);
     if (take) {  // one atomic per wave; lanes take consecutive places in lane order
       const int first = __ffsll((long long)take) - 1;
       int base = 0;
       if (lane == first) base = atomicAdd(&sh.n_out, __popcll(take));
       base = __shfl(base, first, 64);
-      if (k >= thr) out[base + __popcll(take & ((1ull << lane) - 1))] = k;
+      if (mine) out[base + __popcll(take & ((1ull << lane) - 1))] = key[e];
     }
   }
   __syncthreads();
 }
 
-// Keys of chunk `c` of request r, padded with 0: built from the scores (in == nullptr) or copied from in.
-template <int NT>
-__device__ int load_keys(uint64_t* keys, int cap, const float* beam_scores, const float* logp,
-                         const uint64_t* in, long n_in, int n_prev, int n_cand, int r, long base) {
-  const int valid = (int)min((long)cap, n_in - base);
-  if (in == nullptr) {
-    const float* bs = beam_scores + (size_t)r * n_prev;
-    const float* lp = logp + (size_t)r * n_in;
-    for (int i = threadIdx.x; i < cap; i += NT) {
-      uint64_t key = 0;
-      if (i < valid) {
-        const uint32_t f = (uint32_t)(base + i);
-        key = make_key(bs[f / (uint32_t)n_cand] + lp[f], f);
-      }
-      keys[i] = key;
+// One chunk of request r: its K best keys (unordered; all keys, 0-padded, when the chunk holds at most K)
+// to dst[0 .. K).
+__device__ __forceinline__ void reduce_chunk(const float* beam_scores, const float* logp, const uint64_t* src, long n_in,
+                             int n_prev, int n_cand, int r, int c, int K, uint64_t* dst, SelLds& sh) {
+  uint64_t key[kPerThread];
+  const long base = (long)c * kChunk;
+  load_keys(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, base);
+  if (n_in - base <= K) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = e * kThreads + threadIdx.x;
+      if (i < K) dst[i] = key[e];
     }
-  } else {
-    const uint64_t* src = in + (size_t)r * n_in + base;
-    for (int i = threadIdx.x; i < cap; i += NT) keys[i] = i < valid ? src[i] : 0ull;
-  }
-  __syncthreads();
-  return valid;
-}
-
-__global__ __launch_bounds__(kRedThreads) void select_reduce_kernel(const float* __restrict__ beam_scores,
-                                                                    const float* __restrict__ logp,
-                                                                    const uint64_t* __restrict__ in, long n_in,
-                                                                    int n_prev, int n_cand, int nchunk, int K,
-                                                                    uint64_t* __restrict__ out) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(lds);
-  SelShared<kRedThreads>& sh = *reinterpret_cast<SelShared<kRedThreads>*>(keys + kRedChunk);
-  const int r = blockIdx.x / nchunk, c = blockIdx.x - r * nchunk;
-  const int valid = load_keys<kRedThreads>(keys, kRedChunk, beam_scores, logp, in, n_in, n_prev, n_cand, r,
-                                           (long)c * kRedChunk);
-  uint64_t* dst = out + ((size_t)r * nchunk + c) * K;
-  if (valid <= K) {  // keep everything (the padding keys are 0)
-    for (int i = threadIdx.x; i < K; i += kRedThreads) dst[i] = i < kRedChunk ? keys[i] : 0ull;
     return;
   }
-  const uint64_t thr = radix_threshold<kRedThreads>(keys, kRedChunk, K, sh);
-  compact<kRedThreads>(keys, kRedChunk, thr, dst, sh);
+  compact(key, radix_threshold(key, K, sh), dst, sh);
 }
 
-__global__ __launch_bounds__(kFinalThreads) void select_final_kernel(const float* __restrict__ beam_scores,
-                                                                     const float* __restrict__ logp,
-                                                                     const uint64_t* __restrict__ in, long n_in,
-                                                                     int n_prev, int n_cand, int K,
-                                                                     int32_t* parent, int32_t* token,
-                                                                     float* score) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(lds);                 // n_in <= kFinalMax keys
-  uint64_t* best = keys + kFinalMax;                                  // the K survivors, unordered
-  SelShared<kFinalThreads>& sh = *reinterpret_cast<SelShared<kFinalThreads>*>(best + kMaxBeams);
-  const int r = blockIdx.x;
-  const int cap = (int)n_in;
-  load_keys<kFinalThreads>(keys, cap, beam_scores, logp, in, n_in, n_prev, n_cand, r, 0);
-  const uint64_t thr = radix_threshold<kFinalThreads>(keys, cap, K, sh);
-  compact<kFinalThreads>(keys, cap, thr, best, sh);
-  // order: the rank of a survivor is the number of survivors with a larger key (keys are unique, so the ranks
-  // are a permutation of 0 .. K-1); every lane of a wave reads the same survivor at once (an LDS broadcast)
-  uint64_t* sorted = keys;  // the candidate keys are no longer needed
-  int* part = reinterpret_cast<int*>(keys + kMaxBeams);  // partial ranks: two threads per survivor
-  constexpr int kPer = kFinalThreads / 2;
-  for (int i0 = 0; i0 < K; i0 += kPer) {
-    const int i = i0 + (threadIdx.x % kPer), half = threadIdx.x / kPer;
-    const uint64_t mine = i < K ? best[i] : 0ull;
-    const int j0 = half * (K / 2), j1 = half ? K : K / 2;
-    int rank = 0, j = j0;
-    for (; j + 16 <= j1; j += 16) {  // 16 survivors per iteration, 8 loads in flight
-      u32x4_t w[8];
+// Request r's top K of its n_in (<= kChunk) keys, best first, to parent / token / score.
+__device__ __forceinline__ void finish_request(const float* beam_scores, const float* logp, const uint64_t* src, long n_in,
+                               int n_prev, int n_cand, int r, int K, int32_t* parent, int32_t* token,
+                               float* score, SelLds& sh) {
+  uint64_t key[kPerThread];
+  load_keys(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, 0);
+  compact(key, radix_threshold(key, K, sh), sh.best, sh);
+  // order: each wave sorts runs of 64 survivors in registers (a bitonic network over the lanes, largest
+  // first; slots past K hold key 0, which sorts last); then the rank of a survivor is its place in its own
+  // run plus, for every other run, the number of that run's keys above it (a binary search).  Keys are
+  // unique, so the ranks are a permutation of 0 .. K-1.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nrun = (K + 63) >> 6;
+  uint64_t* runs = sh.sorted;
+  for (int run = wave; run < nrun; run += kThreads / 64) {
+    uint64_t x = run * 64 + lane < K ? sh.best[run * 64 + lane] : 0ull;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = reinterpret_cast<const u32x4_t*>(best + j)[u];
+    for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint64_t a = ((uint64_t)w[u].y << 32) | w[u].x, b = ((uint64_t)w[u].w << 32) | w[u].z;
-        rank += (a > mine ? 1 : 0) + (b > mine ? 1 : 0);
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint64_t y = shfl_xor64(x, j);
+        const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+        x = take_max ? (x > y ? x : y) : (x < y ? x : y);
       }
     }
-    for (; j < j1; ++j) rank += best[j] > mine ? 1 : 0;
-    if (half == 1 && i < K) part[threadIdx.x % kPer] = rank;
-    __syncthreads();
-    if (half == 0 && i < K) sorted[rank + part[threadIdx.x]] = mine;
-    __syncthreads();
+    runs[run * 64 + lane] = x;
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrun * 64; i += kThreads) {
+    const uint64_t x = runs[i];
+    const int own = i >> 6;
+    int rank = i & 63;
+    for (int b0 = 0; b0 < nrun; b0 += 8) {  // 8 independent searches in flight
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = b0 + u;
+        if (b < nrun && b != own) {
+          const uint64_t* rb = runs + b * 64;
+          int pos = 0;
+#pragma unroll
+          for (int step = 32; step > 0; step >>= 1)
+            if (rb[pos + step - 1] > x) pos += step;
+          if (pos == 63 && rb[63] > x) pos = 64;
+          rank += pos;
+        }
+      }
+    }
+    if (x != 0ull) sh.best[rank] = x;  // key 0 is padding
+  }
+  __syncthreads();
   // the score is recomputed from its inputs (the same float32 addition), so its sign survives
   const float* bs = beam_scores + (size_t)r * n_prev;
   const float* lp = logp + (size_t)r * n_prev * n_cand;
-  for (int i = threadIdx.x; i < K; i += kFinalThreads) {
-    const uint32_t f = ~(uint32_t)sorted[i];
+  for (int i = threadIdx.x; i < K; i += kThreads) {
+    const uint32_t f = ~(uint32_t)sh.best[i];
     const uint32_t p = f / (uint32_t)n_cand;
     const size_t o = (size_t)r * K + i;
     parent[o] = (int32_t)p;
@@ -254,50 +282,62 @@ __global__ __launch_bounds__(kFinalThreads) void select_final_kernel(const float
   }
 }
 
-size_t reduce_lds_bytes() { return (size_t)kRedChunk * sizeof(uint64_t) + sizeof(SelShared<kRedThreads>); }
-size_t final_lds_bytes() {
-  return (size_t)(kFinalMax + kMaxBeams) * sizeof(uint64_t) + sizeof(SelShared<kFinalThreads>);
+__global__ __launch_bounds__(kThreads, 8) void select_chunk_kernel(const float* __restrict__ beam_scores,
+                                                                const float* __restrict__ logp,
+                                                                const uint64_t* __restrict__ src, long n_in,
+                                                                int n_prev, int n_cand, int nchunk, int K,
+                                                                uint64_t* __restrict__ out) {
+  __shared__ SelLds sh;
+  const int r = blockIdx.x / nchunk, c = blockIdx.x - r * nchunk;
+  reduce_chunk(beam_scores, logp, src, n_in, n_prev, n_cand, r, c, K, out + ((size_t)r * nchunk + c) * K, sh);
 }
+
+__global__ __launch_bounds__(kThreads, 8) void select_finish_kernel(const float* __restrict__ beam_scores,
+                                                                 const float* __restrict__ logp,
+                                                                 const uint64_t* __restrict__ src, long n_in,
+                                                                 int n_prev, int n_cand, int K,
+                                                                 int32_t* parent, int32_t* token, float* score) {
+  __shared__ SelLds sh;
+  finish_request(beam_scores, logp, src, n_in, n_prev, n_cand, blockIdx.x, K, parent, token, score, sh);
+}
+
 }  // namespace
 
 int beam_select_max_beams() { return kMaxBeams; }
 
 size_t beam_select_scratch_bytes(int R, long n, int n_beams) {
-  // keys surviving the first reduce pass, twice (later passes alternate between the two halves)
-  if (n <= kFinalMax) return 0;
-  const long nchunk = (n + kRedChunk - 1) / kRedChunk;
+  // keys surviving the first chunk pass, twice (later passes alternate between the two halves)
+  if (n <= kChunk) return 0;
+  const long nchunk = (n + kChunk - 1) / kChunk;
   return (size_t)2 * R * nchunk * n_beams * sizeof(uint64_t);
 }
 
 hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R, int n_prev, int n_cand,
-                              int n_beams, int32_t* parent, int32_t* token, float* score, void* scratch,
+                              int n_beams, int32_t* parent, int32_t* token, float* score, void* scratch_buf,
                               hipStream_t s) {
   long n = (long)n_prev * n_cand;
-  const int K = n_beams;  // K <= kRedChunk / 4: every reduce pass at least quarters the keys
-  uint64_t* buf[2] = {static_cast<uint64_t*>(scratch), nullptr};
-  if (scratch) buf[1] = buf[0] + (size_t)R * ((n + kRedChunk - 1) / kRedChunk) * K;
+  const int K = n_beams;  // K <= kChunk / 4: every chunk pass at least quarters the keys
+  if (n <= kChunk) {
+    hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)R), dim3(kThreads), 0, s, beam_scores, logp, nullptr,
+                       n, n_prev, n_cand, K, parent, token, score);
+    return hipGetLastError();
+  }
+  const long nchunk0 = (n + kChunk - 1) / kChunk;
+  uint64_t* buf[2] = {static_cast<uint64_t*>(scratch_buf), static_cast<uint64_t*>(scratch_buf) + (size_t)R * nchunk0 * K};
   const uint64_t* in = nullptr;
   int which = 0;
-  while (n > kFinalMax) {
-    const int nchunk = (int)((n + kRedChunk - 1) / kRedChunk);
-    const size_t rlds = reduce_lds_bytes();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_reduce_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)rlds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_reduce_kernel, dim3((unsigned)((size_t)R * nchunk)), dim3(kRedThreads), rlds, s,
-                       beam_scores, logp, in, n, n_prev, n_cand, nchunk, K, buf[which]);
-    e = hipGetLastError();
+  while (n > kChunk) {
+    const int nchunk = (int)((n + kChunk - 1) / kChunk);
+    hipLaunchKernelGGL(select_chunk_kernel, dim3((unsigned)((size_t)R * nchunk)), dim3(kThreads), 0, s, beam_scores,
+                       logp, in, n, n_prev, n_cand, nchunk, K, buf[which]);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     in = buf[which];
     n = (long)nchunk * K;
     which ^= 1;
   }
-  const size_t lds = final_lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_final_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_final_kernel, dim3((unsigned)R), dim3(kFinalThreads), lds, s, beam_scores, logp, in, n,
-                     n_prev, n_cand, K, parent, token, score);
+  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)R), dim3(kThreads), 0, s, beam_scores, logp, in, n, n_prev,
+                     n_cand, K, parent, token, score);
   return hipGetLastError();
 }
 

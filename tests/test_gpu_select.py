@@ -46,7 +46,7 @@ def test_select_matches_oracle(R, n_prev, n_cand, n_beams, ties):
 
 
 def test_select_full_size():
-    """32 requests x 512 beams x 256 candidates -> 512 survivors, as bench.py times it (three passes)."""
+    """32 requests x 512 beams x 256 candidates -> 512 survivors, as bench.py times it (one chunk pass, then the finish)."""
     gu.log("select full size 32 x 512 x 256 -> 512")
     si = inputs.select_inputs(32, 512, 256, seed=0)
     assert_same(si, 512, run_select(si, 512))
@@ -152,3 +152,19 @@ def test_select_random_shapes(i):
     gu.log(f"select random {i}: R={R} n_prev={n_prev} n_cand={n_cand} n_beams={n_beams} ties={ties}")
     si = inputs.select_inputs(R, n_prev, n_cand, seed=20 + i, ties=ties)
     assert_same(si, n_beams, run_select(si, n_beams))
+
+
+def test_select_reused_garbage_scratch():
+    """The scratch's contents are arbitrary on entry: one buffer full of random bytes, reused by several calls
+    (each finding the previous call's survivors), gives the oracle's survivors every time."""
+    dev = gu.device()
+    R, n_prev, n_cand, n_beams = 5, 300, 100, 256
+    need = onela.onela_beam_select_scratch(R, n_prev, n_cand, n_beams)
+    scratch = torch.randint(0, 256, (need,), dtype=torch.uint8, device=dev)
+    for seed in range(3):
+        gu.log(f"select with reused scratch, call {seed}")
+        si = inputs.select_inputs(R, n_prev, n_cand, seed=40 + seed)
+        got = onela.beam_select(torch.from_numpy(si.beam_scores).to(dev), torch.from_numpy(si.logp).to(dev), n_beams,
+                                scratch=scratch)
+        torch.cuda.synchronize()
+        assert_same(si, n_beams, [x.cpu().numpy() for x in got])
