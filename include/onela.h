@@ -189,6 +189,20 @@ onela_status onela_beam_select(int32_t num_requests, int32_t n_prev, int32_t n_c
                                int32_t* d_token, float* d_scores, void* d_scratch, size_t scratch_bytes,
                                void* stream);
 
+/* onela_beam_select without a caller scratch, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, rule, outputs
+ * and errors as onela_beam_select, minus d_scratch / scratch_bytes: the keys that survive a first pass live
+ * in an 8 MiB array the library holds on each GPU for the life of the process (looked up on the first call
+ * on that device; no call allocates).  Selections whose onela_beam_select_scratch exceeds 8 MiB are
+ * rejected with ONELA_ERR_CAPACITY (nothing enqueued): e.g. 32 requests x 512 beams x 256 candidates ->
+ * 512 needs 4 MiB.  Every call on one GPU shares that GPU's array: calls on one GPU must not overlap (two
+ * streams, or two threads, running it at once race and give wrong survivors); calls that follow each other
+ * in stream order are safe.  Nothing in the array needs clearing between calls: every call overwrites what
+ * it reads. */
+onela_status onela_beam_select_noalloc(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                                       const float* d_beam_scores, const float* d_logp, int32_t* d_parent_idx,
+                                       int32_t* d_token, float* d_scores, void* stream);
+
 /* Static text for a status code; message of this thread's last failing call ("" if none). */
 const char* onela_status_string(onela_status s);
 const char* onela_last_error(void);

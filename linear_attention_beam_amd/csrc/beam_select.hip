@@ -21,6 +21,8 @@
 // request needs a device-scope release per workgroup, and on this chip each one writes back the XCD's L2;
 // measured, that costs more than the launch boundary it saves.  Key 0 pads short chunks and ranks below
 // every real key.
+#include <mutex>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -303,6 +305,10 @@ __global__ __launch_bounds__(kThreads, 8) void select_finish_kernel(const float*
 
 }  // namespace
 
+// Library-held scratch of the allocation-free entry point, one copy per GPU (zero-initialised at load).
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 int beam_select_max_beams() { return kMaxBeams; }
 
 size_t beam_select_scratch_bytes(int R, long n, int n_beams) {
@@ -310,6 +316,28 @@ size_t beam_select_scratch_bytes(int R, long n, int n_beams) {
   if (n <= kChunk) return 0;
   const long nchunk = (n + kChunk - 1) / kChunk;
   return (size_t)2 * R * nchunk * n_beams * sizeof(uint64_t);
+}
+
+size_t beam_select_static_max() { return kStaticScratchBytes; }
+
+hipError_t beam_select_static_scratch(void** ptr) {
+  // the array's address on each GPU, looked up once per device with that device current; host code uses
+  // this address only (the array's own name is a host-side stand-in)
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R, int n_prev, int n_cand,

@@ -72,6 +72,10 @@ size_t beam_select_scratch_bytes(int R, long n, int n_beams);
 hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R, int n_prev, int n_cand,
                               int n_beams, int32_t* parent, int32_t* token, float* score, void* scratch,
                               hipStream_t s);
+// The library-held scratch of the allocation-free entry point: its size, and its address on the current
+// device (looked up on the first call per device).
+size_t beam_select_static_max();
+hipError_t beam_select_static_scratch(void** ptr);
 
 hipError_t launch_fullstate(const StepArgs& a, bool bf16, const int32_t* parent, int b_prev, const float* fs_prev,
                             float* fs_next, hipStream_t s);

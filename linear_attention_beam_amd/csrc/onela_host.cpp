@@ -401,6 +401,28 @@ onela_status onela_beam_select(int32_t num_requests, int32_t n_prev, int32_t n_c
   return st != ONELA_OK ? st : ok();
 }
 
+onela_status onela_beam_select_noalloc(int32_t num_requests, int32_t n_prev, int32_t n_cand, int32_t n_beams,
+                                       const float* d_beam_scores, const float* d_logp, int32_t* d_parent_idx,
+                                       int32_t* d_token, float* d_scores, void* stream) {
+  onela_status st = select_args(num_requests, n_prev, n_cand, n_beams);
+  if (st != ONELA_OK) return st;
+  if (!d_beam_scores || !d_logp || !d_parent_idx || !d_token || !d_scores)
+    return fail(ONELA_ERR_INVALID_ARG, "a beam-selection buffer is NULL");
+  const size_t need = beam_select_scratch_bytes(num_requests, (long)n_prev * n_cand, n_beams);
+  if (need > beam_select_static_max())
+    return fail(ONELA_ERR_CAPACITY, "selection needs %zu bytes of scratch, above the %zu the library holds", need,
+                beam_select_static_max());
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = beam_select_static_scratch(&scratch);
+    if (e != hipSuccess) return fail(ONELA_ERR_DEVICE, "static scratch lookup: %s", hipGetErrorString(e));
+  }
+  st = launched(launch_beam_select(d_beam_scores, d_logp, num_requests, n_prev, n_cand, n_beams, d_parent_idx,
+                                   d_token, d_scores, scratch, static_cast<hipStream_t>(stream)),
+                "beam selection");
+  return st != ONELA_OK ? st : ok();
+}
+
 const char* onela_status_string(onela_status s) {
   switch (s) {
     case ONELA_OK: return "ONELA_OK";

@@ -66,6 +66,8 @@ _SIGNATURES = {
                                   ctypes.POINTER(ctypes.c_size_t)],
     "onela_beam_select": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P],
+    "onela_beam_select_noalloc": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                                  _P, _P],
     "onela_status_string": [ctypes.c_int],
     "onela_last_error": [],
 }
@@ -160,6 +162,12 @@ def onela_beam_select(R: int, n_prev: int, n_cand: int, n_beams: int, beam_score
                       stream: int) -> None:
     _check(lib().onela_beam_select(R, n_prev, n_cand, n_beams, beam_scores_ptr, logp_ptr, parent_ptr, token_ptr,
                                    scores_ptr, scratch_ptr, scratch_bytes, stream), "onela_beam_select")
+
+
+def onela_beam_select_noalloc(R: int, n_prev: int, n_cand: int, n_beams: int, beam_scores_ptr: int, logp_ptr: int,
+                              parent_ptr: int, token_ptr: int, scores_ptr: int, stream: int) -> None:
+    _check(lib().onela_beam_select_noalloc(R, n_prev, n_cand, n_beams, beam_scores_ptr, logp_ptr, parent_ptr,
+                                           token_ptr, scores_ptr, stream), "onela_beam_select_noalloc")
 
 
 # ---------------------------------------------------------------------------------------------------
