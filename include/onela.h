@@ -123,7 +123,9 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
 /* Free the host handle.  The workspace stays the caller's; wait for the stream first. */
 onela_status onela_destroy(onela_handle h);
 
-/* Install the shared post-prefill state: d_sctx is [R][H][d_v][d_k] float32 on the device.  It is
+/* Install the shared post-prefill state that every beam of a request starts from ("Scientific Impact
+ * Assessment: OneLA", §1 Core Contribution, mechanism (1): one S_ctx per request and head; OneLA index page,
+ * Abstract: a single shared prompt-derived state).  d_sctx is [R][H][d_v][d_k] float32 on the device.  It is
  * copied (transposed, and split into bf16 high and low parts for the fused kernel), so the caller may
  * reuse d_sctx once the stream has passed this call.  Starts a new decode (t = 0). */
 onela_status onela_set_context(onela_handle h, const float* d_sctx, void* stream);
@@ -141,8 +143,13 @@ onela_status onela_set_context(onela_handle h, const float* d_sctx, void* stream
 onela_status onela_prefill(onela_handle h, int32_t n_tokens, const float* d_k, const float* d_v,
                            const float* d_alpha, const float* d_beta, float* d_sctx_out, void* stream);
 
-/* One decode step for every request and head (projection replay in REPLAY mode; dense update in
- * FULLSTATE mode).  n_beams in 1..max_beams new beams per request:
+/* One decode step for every request and head ("Scientific Impact Assessment: OneLA", §1 Core Contribution,
+ * mechanisms (1)-(3), and the fused kernel that reuses S_ctx across beams; OneLA index page, Abstract).  In
+ * REPLAY mode each beam's S_{t-1} k and S_t q come from the decayed S_ctx contraction plus a replay of the
+ * records on the beam's chain (mechanism (2): only two vector projections of the state, never the matrix);
+ * the new record (alpha, k, u = beta (v - alpha S_{t-1} k)) is appended (mechanism (1)) and the chain table
+ * extended through the parents (mechanism (3)).  FULLSTATE mode keeps a dense state per beam instead (the
+ * controlled comparison of §2 Methodological Rigor).  n_beams in 1..max_beams new beams per request:
  *   d_q, d_k    [R][n_beams][H][d_k]  qkv_dtype
  *   d_v         [R][n_beams][H][d_v]  qkv_dtype
  *   d_alpha     [R][n_beams][H]       float32 (decay, usually in (0, 1])
@@ -156,10 +163,18 @@ onela_status onela_step(onela_handle h, int32_t n_beams, const void* d_q, const 
                         const void* d_v, const float* d_alpha, const float* d_beta,
                         const int32_t* d_parent_idx, float* d_o, void* stream);
 
-/* Drop every record and chain (logically) and return to t = 0 on the same context. */
+/* Drop every record and chain (logically) and return to t = 0 on the same context: records sit where they
+ * were written and are never moved ("Scientific Impact Assessment: OneLA", §1 Core Contribution, mechanism
+ * (3): immutable physical record placement), so a new decode only restarts the step counter and the chain
+ * tables; no device work is enqueued and the stream argument is accepted for symmetry.  Also clears the
+ * parent-error flag for the new decode. */
 onela_status onela_reset(onela_handle h, void* stream);
 
-/* Wait for the stream, then report the sticky device flag: ONELA_OK or ONELA_ERR_BAD_PARENT. */
+/* Wait for the stream, then report the sticky device flag of the current decode: ONELA_OK, or
+ * ONELA_ERR_BAD_PARENT if some step named a parent outside the previous step's beams (a chain the ancestry
+ * index of "Scientific Impact Assessment: OneLA", §1 Core Contribution, mechanism (3), cannot follow; that
+ * step's outputs for the beam are then computed from parent 0).  Returns ONELA_ERR_DEVICE if the stream
+ * fails. */
 onela_status onela_get_status(onela_handle h, void* stream);
 
 /* Fill *view with the current decode state (host-side only; no synchronisation). */
