@@ -2,18 +2,24 @@
 """Benchmark of the large-beam Gated DeltaNet decode step on one MI355X.
 
 One bench "step" is one whole decode of the workload: L onela_step calls (ancestry index update, shared
-S_ctx contraction, key and query replay, record append, output: one fused kernel per call) over
-R requests x B beams x H heads, after onela_reset.  Inputs (all L steps) and the context are resident in
-HBM before timing starts.  value = beam-tokens per second = R * B * L / seconds per decode.
+S_ctx contraction, key and query replay, record append, output: at step 1 one fused kernel, later an
+ancestry-plan kernel and the fused kernel) over R requests x B beams x H heads, after onela_reset.  Inputs
+(all L steps) and the context are resident in HBM before timing starts.  value = beam-tokens per second =
+R * B * L / (median seconds per decode over the timed decodes).
 
 Prints one JSON line.  Extra objects:
-  roofline      the fused step kernel: algorithmic HBM bytes per launch (compulsory traffic, counted from
-                the run's own chain tables) / its average launch time from HIP events in the timed region
-  cpu_baseline  the float64 CPU oracle (record-replay form) timed on whole requests of the same workload
+  roofline      one onela_step (its two kernels): algorithmic HBM bytes per step (compulsory traffic, counted
+                from the run's own chain tables) / the step's median time from HIP events on its stream in the
+                timed region
+  configs       the same measurement (decode time, rate, bytes, fraction, FullState speed-up, CPU oracle) for
+                each workload of the table (default: the four GPU-sized workloads, the headline one included)
+  cpu_baseline  the float64 CPU oracle (record-replay form) timed on (request, head) pairs of the same
+                workload, scaled to beam-tokens/s of whole requests
   fullstate     the controlled FullState path (dense per-beam state) on the same inputs
   materialize   the materializing-replay path (each beam's dense parent state rebuilt every step) on the same
                 inputs
-  hbm_probe     copy and fill bandwidth of plain torch kernels on the same GPU (context for the fraction)
+  hbm_probe     read-only, 2:3 read:write mix, copy and write-only bandwidth of plain streaming kernels
+                (libonela_probe.so) on the same GPU (context for the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
   prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the dense
@@ -40,7 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector: 256 CUs x 64 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
+FP32_PEAK_TFLOPS = 78.6      # MI355X fp32 vector without packed FP32: 256 CUs x 64 lanes x 2 (FMA) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.json")
 FUSED_SRC = os.path.join(ROOT, "linear_attention_beam_amd", "csrc", "step_fused.hip")
 
@@ -85,27 +91,47 @@ def algorithmic_bytes(cfg, chains, parents):
 
 
 def hbm_probe(torch, dev, gib: float = 2.0):
-    """Achievable HBM bandwidth with plain torch kernels on this GPU: copy (1 read + 1 write) and fill (write
-    only), best of 5.  Context for the roofline fraction; not part of the timed decode."""
-    n = int(gib * (1 << 30)) // 4
-    x = torch.ones(n, dtype=torch.float32, device=dev)
-    y = torch.empty_like(x)
+    """Bandwidth of plain streaming kernels (libonela_probe.so, 16-byte accesses) on this GPU, best of 5 each:
+    read-only, the 2:3 read:write mix of the decode step, copy (1:1) and write-only.  Context for the roofline
+    fraction (whose peak stays the published 8 TB/s); not part of the timed decode."""
+    import ctypes
+    path = os.path.join(ROOT, "linear_attention_beam_amd", "lib", "libonela_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m linear_attention_beam_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.onela_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.onela_probe_stream.restype = ctypes.c_int
+    n = int(gib * (1 << 30)) // 16                      # 16-byte elements per stream
+    src = torch.ones(2 * n * 4, dtype=torch.float32, device=dev)
+    dst = torch.empty(3 * n * 4, dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid = cus * 32  # the best of 4, 8, 16 and 32 workgroups per CU in a sweep of these kernels
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
 
-    def best(fn, nbytes):
-        fn()
+    def best(mode, nbytes):
+        def run():
+            rc = lib.onela_probe_stream(src.data_ptr(), dst.data_ptr(), n, mode, sink.data_ptr(), grid,
+                                        stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"onela_probe_stream mode {mode} failed ({rc})")
+        run()
         torch.cuda.synchronize()
         out = 0.0
         for _ in range(5):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
+            a.record(stream)
+            run()
+            b.record(stream)
             torch.cuda.synchronize()
             out = max(out, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
         return out
 
-    res = {"copy_GBs": best(lambda: y.copy_(x), 8.0 * n), "fill_GBs": best(lambda: y.fill_(2.0), 4.0 * n)}
-    del x, y
+    res = {"read_GBs": best(0, 32.0 * n), "mix_2r3w_GBs": best(1, 80.0 * n), "copy_GBs": best(2, 32.0 * n),
+           "write_GBs": best(3, 16.0 * n), "bytes_per_stream": 16 * n,
+           "kernel": "onela_probe_stream (16-byte loads/stores, grid-stride, 32 workgroups x 256 threads per CU)"}
+    del src, dst, sink
     return res
 
 
@@ -146,8 +172,10 @@ def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool
     (two FMAs per state element), sequential over tokens.  For d_k = 128 and d_v in {16, 32, 64, 128, 256} the
     library runs it in chunked form on the matrix cores: per 32-token chunk and head, G = K K^T (lower 16 x 16
     blocks, 3 x 16 x 16 x 128, once per chunk), Y = K S^T (32 x d_v x 128), U = T X (32 x d_v x 32) and the
-    state update (128 x d_v x 32), each as three bf16 products (high/low halves): that MFMA work against the
-    bf16 peak is the roofline; the rate of the equivalent float32 recurrence is reported beside it."""
+    state update (128 x d_v x 32), each as three bf16 products (high/low halves).  The roofline counts the
+    method's own work (the recurrence's 4 d_k d_v FLOPs per token and head) against the bf16 MFMA peak; the
+    MFMA products actually issued (the chunked form's extra work and the three-way split) are reported beside
+    it as mfma_issued."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ctx.prefill(*ctx_in)
     torch.cuda.synchronize()
@@ -161,20 +189,24 @@ def prefill_bench(torch, ctx, ctx_in, cfg, stream, reps: int = 5, with_cpu: bool
     flops = 4.0 * cfg.d_k * cfg.d_v * N * heads
     nbytes = 4.0 * heads * N * (cfg.d_k + cfg.d_v + 2) + 4.0 * heads * cfg.d_k * cfg.d_v * 3
     chunked = cfg.d_k == 128 and cfg.d_v in (16, 32, 64, 128, 256)
+    achieved = flops / (ms * 1e-3) / 1e12
     if chunked:
         chunks = -(-N // 32)
         per_chunk = 3 * 2.0 * (3 * 16 * 16 * 128 + 32 * cfg.d_v * 128 + 32 * cfg.d_v * 32 + 128 * cfg.d_v * 32)
         mfma_flops = per_chunk * chunks * heads
         roof = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 (high/low halves)",
-                "achieved": mfma_flops / (ms * 1e-3) / 1e12,
-                "frac": mfma_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "mfma_flops": mfma_flops}
+                "work": "4 d_k d_v FLOPs per token and head (the recurrence's own work)",
+                "achieved": achieved, "frac": achieved / BF16_PEAK_TFLOPS,
+                "mfma_issued_flops": mfma_flops, "mfma_issued_TFLOPs": mfma_flops / (ms * 1e-3) / 1e12,
+                "mfma_issued_frac": mfma_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     else:
         roof = {"bound": "alu", "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
+                "work": "4 d_k d_v FLOPs per token and head", "achieved": achieved,
+                "frac": achieved / FP32_PEAK_TFLOPS}
     out = {"shape": f"R={cfg.R} H={cfg.H} N={N} d_k={cfg.d_k} d_v={cfg.d_v}", "ms_per_call": ms,
            "kernel": "chunked MFMA" if chunked else "row-parallel fp32",
            "tokens_per_s": cfg.R * N / (ms * 1e-3), "fp32_flops": flops,
-           "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "achieved_TFLOPs": achieved,
            "roofline": roof,
            "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
            "note": "call time: the prefill kernels plus the state's transpose and bf16 split"}
@@ -218,7 +250,8 @@ def stack_bench(torch, cfg, layers: int, step_ms: float, reps: int = 3):
 
 
 def cpu_baseline(cfg, steps, budget_s: float):
-    """Time the CPU oracle's record-replay decode on whole requests (every head, beam and step)."""
+    """Time the CPU oracle's record-replay decode on (request, head) pairs of the workload (every beam and step
+    of each pair), as many as fit the budget (at least one), scaled to beam-tokens/s of whole requests."""
     import oracle
     from linear_attention_beam_amd import inputs
     try:
@@ -228,40 +261,206 @@ def cpu_baseline(cfg, steps, budget_s: float):
     except Exception:  # noqa: BLE001
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
+    f = inputs.bf16_bits_to_f32 if cfg.qkv_dtype == "bf16" else (lambda x: x)
 
     def head_steps(r, h):
-        f = inputs.bf16_bits_to_f32 if cfg.qkv_dtype == "bf16" else (lambda x: x)
         return [dict(q=f(s.q[r, :, h])[None, :, None], k=f(s.k[r, :, h])[None, :, None],
                      v=f(s.v[r, :, h])[None, :, None], alpha=s.alpha[r, :, h][None, :, None],
                      beta=s.beta[r, :, h][None, :, None], parent=s.parent[r][None]) for s in steps]
 
     # The decode's cost does not depend on the values of S_ctx, so the state comes from the seeded generator
-    # (same shape) rather than from a float64 prefill of 5120 tokens per head, which would dominate the run.
+    # (same shape) rather than from a float64 prefill of the prompt, which would dominate the run.
     sctx_all = inputs.direct_sctx(dataclasses.replace(cfg, sctx_std=0.1))
-    elapsed, reqs = 0.0, 0
-    while reqs < cfg.R and (reqs == 0 or elapsed < budget_s):
-        r = reqs
-        hs = [head_steps(r, h) for h in range(cfg.H)]
+    elapsed, pairs = 0.0, 0
+    while pairs < cfg.R * cfg.H and (pairs == 0 or elapsed < budget_s):
+        r, h = divmod(pairs, cfg.H)
+        hs = head_steps(r, h)
         t0 = time.perf_counter()
-        for h in range(cfg.H):
-            oracle.decode_replay(sctx_all[r, h][None, None], hs[h], cfg.B, cfg.L)
+        oracle.decode_replay(sctx_all[r, h][None, None], hs, cfg.B, cfg.L)
         elapsed += time.perf_counter() - t0
-        reqs += 1
-    return {"value": reqs * cfg.B * cfg.L / elapsed, "unit": "beam-tokens/s", "cores": cores,
+        pairs += 1
+    return {"value": pairs * cfg.B * cfg.L / cfg.H / elapsed, "unit": "beam-tokens/s", "cores": cores,
             "blas_threads": blas_threads, "kind": "oracle",
-            "sample": f"requests 0..{reqs - 1} of {cfg.R}: every head, beam and decode step (record-replay form, "
-                      f"float64 numpy; S_ctx of the same shape from the seeded generator)",
+            "sample": f"{pairs} of {cfg.R * cfg.H} (request, head) pairs, each with every beam and decode step "
+                      f"(record-replay form, float64 numpy; S_ctx of the same shape from the seeded generator); "
+                      f"rate = pairs x B x L / H / seconds",
             "seconds": round(elapsed, 3)}
+
+
+def upload(torch, dev, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def traffic_of(config_index: int):
+    """HBM bytes per step from the committed counter runs, if they were taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    tr = json.load(open(TRAFFIC_FILE))
+    key = f"config{config_index}"
+    if tr.get("kernel_hash") == kernel_source_hash() and key in tr.get("configs", {}):
+        return tr["configs"][key]["bytes_per_launch"]
+    return None
+
+
+def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
+    """Decode benchmark of one workload: the context from a GPU prefill of the workload's prompt, W warm-up
+    decodes, then K timed decodes with HIP events around every decode and every step on the stream the steps
+    run on.  Returns the per-config record and, for the headline workload, the objects the rest of the line
+    needs."""
+    cfg = inputs.config(index)
+    t0 = time.time()
+    steps = inputs.decode_inputs(cfg)
+    pf = inputs.prefill_inputs(cfg) if cfg.prefill_steps else None
+    log(f"[bench] config{index} {cfg.name}: inputs generated in {time.time() - t0:.1f}s")
+    dsteps = [dict(q=upload(torch, dev, s.q), k=upload(torch, dev, s.k), v=upload(torch, dev, s.v),
+                   alpha=upload(torch, dev, s.alpha), beta=upload(torch, dev, s.beta),
+                   parent=upload(torch, dev, s.parent)) for s in steps]
+    outs = [torch.empty((cfg.R, cfg.B, cfg.H, cfg.d_v), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
+    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype,
+                      tile_beams=args.tile_beams if headline else 0, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ctx_in = ([upload(torch, dev, pf.k), upload(torch, dev, pf.v), upload(torch, dev, pf.alpha),
+               upload(torch, dev, pf.beta)] if pf is not None else [upload(torch, dev, inputs.direct_sctx(cfg))])
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    if pf is not None:
+        ctx.prefill(*ctx_in)
+    else:
+        ctx.set_context(*ctx_in)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    extra = {"context_ms": e0.elapsed_time(e1)}
+    if headline and pf is not None:
+        extra["prefill"] = prefill_bench(torch, ctx, ctx_in, cfg, stream, with_cpu=not args.no_cpu_baseline)
+        log(f"[bench] prefill: {extra['prefill']['ms_per_call']:.3f} ms/call, "
+            f"{extra['prefill']['achieved_TFLOPs']:.1f} TFLOP/s of the recurrence's own work")
+    del ctx_in
+
+    def decode(events=None):
+        ctx.reset()
+        for t in range(cfg.L):
+            if events is not None:
+                events[t][0].record(stream)
+            ctx.step(**dsteps[t], out=outs[t])
+            if events is not None:
+                events[t][1].record(stream)
+
+    for _ in range(args.warmup):
+        decode()
+    torch.cuda.synchronize()
+    if ctx.status() != onela.ONELA_OK:
+        raise RuntimeError("device flag: parent index out of range")
+    view = ctx.view()
+    chains = view["chains"].cpu().numpy()
+    per_step_bytes = algorithmic_bytes(cfg, chains, [s.parent for s in steps])
+
+    K = args.steps
+    step_events = [[[ev(), ev()] for _ in range(cfg.L)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        decode(step_events[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) / K
+    step_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in step_events])     # [K, L]
+    # a decode spans from its first step's start to its last step's end (onela_reset enqueues nothing)
+    decode_ms = np.array([row[0][0].elapsed_time(row[-1][1]) for row in step_events])
+    ms = float(np.median(decode_ms))
+    step_med = np.median(step_ms, axis=0)                                                    # [L]
+    # the roofline's time: the median decode's steps (the step of each launch pair, its gaps excluded)
+    step_sum = float(np.median(step_ms.sum(axis=1)))
+    achieved = sum(per_step_bytes) / (step_sum * 1e-3) / 1e9
+    mfma_flops = 8.0 * cfg.d_v * cfg.d_k * cfg.R * cfg.B * cfg.H * cfg.L   # (k and q) x (hi and lo) x 2 flops
+    traffic = traffic_of(index)
+    rec = {
+        "workload": cfg.name,
+        "ms_per_step": ms,
+        "beam_tokens_per_s": cfg.beam_tokens / (ms * 1e-3),
+        "decode_ms_min_max": [float(decode_ms.min()), float(decode_ms.max())],
+        "algorithmic_bytes_per_launch": sum(per_step_bytes) / cfg.L,
+        "algorithmic_bytes_by_decode_step": per_step_bytes,
+        "step_us_by_decode_step": [round(float(x) * 1e3, 2) for x in step_med],
+        "achieved_GBs": achieved,
+        "frac": achieved / HBM_PEAK_GBS,
+        "traffic_bytes_per_launch": (sum(traffic) / len(traffic)) if traffic else None,
+        "mfma_frac": mfma_flops / (step_sum * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "wall_ms_per_decode": wall * 1e3,
+    }
+    log(f"[bench] config{index}: {ms:.4f} ms/decode (median of {K}), {rec['beam_tokens_per_s']:.4g} beam-tokens/s, "
+        f"{achieved:.0f} GB/s = {rec['frac']:.3f} of peak; steps {rec['step_us_by_decode_step']} us")
+    sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
+    del view
+    if headline:
+        extra.update(ctx=ctx, steps=steps, dsteps=dsteps, outs=outs, cfg=cfg, sctx_host=sctx_host, stream=stream,
+                     step_ms=step_ms, chains=chains)
+    else:
+        ctx.close()
+        del ctx
+
+    if not args.no_fullstate:
+        fs = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, mode="fullstate",
+                         device=dev)
+        fs.set_context(torch.from_numpy(sctx_host).to(dev))
+
+        def fs_decode():
+            fs.reset()
+            for t in range(cfg.L):
+                fs.step(**dsteps[t], out=outs[t])
+
+        fs_decode()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a, b = ev(), ev()
+            a.record(stream)
+            fs_decode()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        fs_ms = float(np.median(times))
+        rec["fullstate_ms_per_step"] = fs_ms
+        rec["fullstate_speedup"] = fs_ms / ms
+        if headline:
+            fs_bytes = 2.0 * cfg.R * cfg.B * cfg.H * cfg.d_k * cfg.d_v * 4 * cfg.L
+            # compulsory: each distinct parent's state read once per step, every child's state written once
+            st_bytes = cfg.H * cfg.d_k * cfg.d_v * 4.0
+            fs_compulsory = sum(st_bytes * (len(np.unique(s.parent[r])) + s.parent.shape[1])
+                                for s in steps for r in range(cfg.R))
+            extra["fullstate"] = {
+                "ms_per_step": fs_ms, "beam_tokens_per_s": cfg.beam_tokens / (fs_ms * 1e-3),
+                "state_bytes_per_decode": fs_bytes, "achieved_GBs": fs_bytes / (fs_ms * 1e-3) / 1e9,
+                "compulsory_bytes_per_decode": fs_compulsory,
+                "compulsory_GBs": fs_compulsory / (fs_ms * 1e-3) / 1e9,
+                "note": "state_bytes counts every child's read of its parent's state; siblings share it through the "
+                        "caches, so compulsory_bytes counts each distinct parent once",
+                "replay_speedup": fs_ms / ms}
+        log(f"[bench] config{index} FullState: {fs_ms:.3f} ms/decode; replay is {fs_ms / ms:.1f}x faster")
+        fs.close()
+        del fs
+
+    if not args.no_cpu_baseline:
+        budget = args.cpu_budget if headline else args.cpu_budget / 3
+        rec["cpu_baseline"] = cpu_baseline(cfg, steps, budget)
+        log(f"[bench] config{index} CPU oracle: {rec['cpu_baseline']['value']:.4g} beam-tokens/s "
+            f"({rec['cpu_baseline']['seconds']} s)")
+    return rec, extra
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20, help="timed decodes")
+    ap.add_argument("--steps", type=int, default=20, help="timed decodes per workload")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload index (default 3: R=32 H=16 B=512 L=8)")
+    ap.add_argument("--config", type=int, default=3, help="headline workload (default 3: R=32 H=16 B=512 L=8)")
+    ap.add_argument("--table-configs", default="1,2,3,4",
+                    help="workloads of the per-config table (comma-separated indices, or 'none')")
     ap.add_argument("--tile-beams", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU-baseline work")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of CPU-oracle work for the headline workload (a third of it for each other one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullstate", action="store_true")
     ap.add_argument("--no-select", action="store_true", help="skip the beam-selection measurement")
@@ -285,7 +484,6 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    cfg = inputs.config(args.config)
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -293,94 +491,13 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    log(f"[bench] workload: {cfg.name}")
-    t0 = time.time()
-    steps = inputs.decode_inputs(cfg)
-    pf = inputs.prefill_inputs(cfg) if cfg.prefill_steps else None
-    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
 
-    def up(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    dsteps = [dict(q=up(s.q), k=up(s.k), v=up(s.v), alpha=up(s.alpha), beta=up(s.beta), parent=up(s.parent))
-              for s in steps]
-    outs = [torch.empty((cfg.R, cfg.B, cfg.H, cfg.d_v), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
-
-    ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype,
-                      tile_beams=args.tile_beams, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    e0, e1 = ev(), ev()
-    ctx_in = [up(pf.k), up(pf.v), up(pf.alpha), up(pf.beta)] if pf is not None else [up(inputs.direct_sctx(cfg))]
-    torch.cuda.synchronize()
-    e0.record(stream)
-    if pf is not None:
-        ctx.prefill(*ctx_in)
-    else:
-        ctx.set_context(*ctx_in)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    context_ms = e0.elapsed_time(e1)
-    log(f"[bench] context ready ({'prefill ' + str(cfg.prefill_steps) + ' tokens' if pf else 'set_context'}: "
-        f"{context_ms:.2f} ms)")
-    prefill_line = None
-    if pf is not None:
-        prefill_line = prefill_bench(torch, ctx, ctx_in, cfg, stream, with_cpu=not args.no_cpu_baseline)
-        log(f"[bench] prefill: {prefill_line['ms_per_call']:.3f} ms/call, {prefill_line['achieved_TFLOPs']:.1f} "
-            f"TFLOP/s fp32")
-    del ctx_in
-
-    def decode(events=None):
-        ctx.reset()
-        for t in range(cfg.L):
-            if events is not None:
-                events[t][0].record(stream)
-            ctx.step(**dsteps[t], out=outs[t])
-            if events is not None:
-                events[t][1].record(stream)
-
-    for _ in range(args.warmup):
-        decode()
-    torch.cuda.synchronize()
-    if ctx.status() != onela.ONELA_OK:
-        raise RuntimeError("device flag: parent index out of range")
-    view = ctx.view()
-    chains = view["chains"].cpu().numpy()
-    per_launch_bytes = algorithmic_bytes(cfg, chains, [s.parent for s in steps])
-    log(f"[bench] warmup done; algorithmic bytes per decode {sum(per_launch_bytes) / 1e9:.3f} GB")
-
-    launch_events = [[[ev(), ev()] for _ in range(cfg.L)] for _ in range(args.steps)]
-    start, stop = ev(), ev()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for k in range(args.steps):
-        decode(launch_events[k])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    kernel_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in launch_events])  # [K, L]
-    kernel_avg_ms = float(kernel_ms.mean())
-    achieved = sum(per_launch_bytes) / (kernel_ms.sum(axis=1).mean() * 1e-3) / 1e9
-    value = cfg.beam_tokens / (ms_per_step * 1e-3)
-    log(f"[bench] {args.steps} decodes: {ms_per_step:.4f} ms/decode (wall {wall / args.steps * 1e3:.4f}), "
-        f"{value:.4g} beam-tokens/s; fused kernel avg {kernel_avg_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
-    per_step_us = [round(float(x) * 1e3, 2) for x in kernel_ms.mean(axis=0)]
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        key = f"config{args.config}"
-        if tr.get("kernel_hash") == kernel_source_hash() and key in tr.get("configs", {}):
-            traffic = tr["configs"][key]["bytes_per_launch"]
-    mfma_flops = 8.0 * cfg.d_v * cfg.d_k * cfg.R * cfg.B * cfg.H * cfg.L   # (k and q) x (hi and lo) x 2 flops
+    rec, extra = measure_config(torch, onela, inputs, dev, args.config, args, headline=True)
+    cfg, ctx = extra["cfg"], extra["ctx"]
+    ms_per_step = rec["ms_per_step"]
     line = {
         "metric": "beam-tokens/sec of GDN beam-decode step",
-        "value": value,
+        "value": rec["beam_tokens_per_s"],
         "unit": "beam-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -394,72 +511,37 @@ def main():
         "config": {"workload": cfg.name, "requests": cfg.R, "heads": cfg.H, "d_k": cfg.d_k, "d_v": cfg.d_v,
                    "beams": cfg.B, "decode_steps": cfg.L, "prefill_tokens": cfg.prefill_steps,
                    "beam_tokens_per_step": cfg.beam_tokens, "tile_beams": args.tile_beams or "auto"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (sum(traffic) / len(traffic)) if traffic else None,
-                     "kernel": "onela::step_fused_kernel",
-                     "algorithmic_bytes_per_launch": sum(per_launch_bytes) / cfg.L,
-                     "kernel_avg_us": kernel_avg_ms * 1e3, "kernel_us_by_decode_step": per_step_us,
-                     "mfma_frac": mfma_flops / (kernel_ms.sum(axis=1).mean() * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
-        "context_ms": context_ms,
+        "roofline": {"bound": "hbm", "achieved": rec["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": rec["frac"], "traffic": rec["traffic_bytes_per_launch"],
+                     "kernel": "onela_step: ancestry_plan_kernel (steps >= 2) + step_fused_kernel",
+                     "algorithmic_bytes_per_launch": rec["algorithmic_bytes_per_launch"],
+                     "kernel_avg_us": float(np.mean(rec["step_us_by_decode_step"])),
+                     "kernel_us_by_decode_step": rec["step_us_by_decode_step"],
+                     "timing": "HIP events around each onela_step on its stream; median over the timed decodes",
+                     "mfma_frac": rec["mfma_frac"]},
+        "context_ms": extra["context_ms"],
         # recurrent state kept per (beam, head) after the last step: a dense fp32 matrix (FullState) against the
         # records appended along one chain (one per step: k in the input dtype, u fp32, alpha fp32)
         "state_capacity": {"fullstate_bytes": cfg.d_v * cfg.d_k * 4,
                            "records_bytes": cfg.L * (cfg.d_k * cfg.in_bytes + 4 * cfg.d_v + 4),
                            "ratio": cfg.d_v * cfg.d_k * 4 / (cfg.L * (cfg.d_k * cfg.in_bytes + 4 * cfg.d_v + 4))},
     }
-    if prefill_line is not None:
-        line["prefill"] = prefill_line
+    if "prefill" in extra:
+        line["prefill"] = extra["prefill"]
+    if "fullstate" in extra:
+        line["fullstate"] = extra["fullstate"]
     line["hbm_probe"] = hbm_probe(torch, dev)
+    log(f"[bench] probes: read {line['hbm_probe']['read_GBs']:.0f}, 2:3 mix {line['hbm_probe']['mix_2r3w_GBs']:.0f}, "
+        f"copy {line['hbm_probe']['copy_GBs']:.0f}, write {line['hbm_probe']['write_GBs']:.0f} GB/s")
     if not args.no_select:
         line["beam_select"] = select_bench(torch, dev, cfg, with_cpu=not args.no_cpu_baseline)
         log(f"[bench] beam selection {line['beam_select']['shape']}: {line['beam_select']['us_per_call']:.1f} us/call")
-    sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
-    del view
-    ctx.close()
-    del ctx
-
-    if not args.no_fullstate:
-        fs = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, mode="fullstate",
-                         device=dev)
-        fs.set_context(torch.from_numpy(sctx_host).to(dev))
-
-        def fs_decode():
-            fs.reset()
-            for t in range(cfg.L):
-                fs.step(**dsteps[t], out=outs[t])
-
-        fs_decode()
-        torch.cuda.synchronize()
-        reps = 3
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(reps):
-            fs_decode()
-        b.record(stream)
-        torch.cuda.synchronize()
-        fs_ms = a.elapsed_time(b) / reps
-        fs_bytes = 2.0 * cfg.R * cfg.B * cfg.H * cfg.d_k * cfg.d_v * 4 * cfg.L
-        # compulsory: each distinct parent's state read once per step, every child's state written once
-        st_bytes = cfg.H * cfg.d_k * cfg.d_v * 4.0
-        fs_compulsory = sum(st_bytes * (len(np.unique(s.parent[r])) + s.parent.shape[1])
-                            for s in steps for r in range(cfg.R))
-        line["fullstate"] = {"ms_per_step": fs_ms, "beam_tokens_per_s": cfg.beam_tokens / (fs_ms * 1e-3),
-                             "state_bytes_per_decode": fs_bytes,
-                             "achieved_GBs": fs_bytes / (fs_ms * 1e-3) / 1e9,
-                             "compulsory_bytes_per_decode": fs_compulsory,
-                             "compulsory_GBs": fs_compulsory / (fs_ms * 1e-3) / 1e9,
-                             "note": "state_bytes counts every child's read of its parent's state; siblings share "
-                                     "it through the caches, so compulsory_bytes counts each distinct parent once",
-                             "replay_speedup": fs_ms / ms_per_step}
-        log(f"[bench] FullState: {fs_ms:.3f} ms/decode; replay is {fs_ms / ms_per_step:.1f}x faster")
-        fs.close()
-        del fs
 
     if not args.no_materialize:
+        stream, dsteps, outs = extra["stream"], extra["dsteps"], extra["outs"]
         mz = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, materialize=True,
                          device=dev)
-        mz.set_context(torch.from_numpy(sctx_host).to(dev))
+        mz.set_context(torch.from_numpy(extra["sctx_host"]).to(dev))
 
         def mz_decode():
             mz.reset()
@@ -468,14 +550,15 @@ def main():
 
         mz_decode()
         torch.cuda.synchronize()
-        reps = 3
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(reps):
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
             mz_decode()
-        b.record(stream)
-        torch.cuda.synchronize()
-        mz_ms = a.elapsed_time(b) / reps
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        mz_ms = float(np.median(times))
         flops = sum(2.0 * cfg.R * cfg.B * cfg.H * cfg.d_k * cfg.d_v * (t + 2) for t in range(cfg.L))
         line["materialize"] = {"ms_per_step": mz_ms, "beam_tokens_per_s": cfg.beam_tokens / (mz_ms * 1e-3),
                                "fp32_flops_per_decode": flops, "achieved_TFLOPs": flops / (mz_ms * 1e-3) / 1e12,
@@ -484,6 +567,8 @@ def main():
             "faster")
         mz.close()
         del mz
+    ctx.close()
+    del ctx, extra
 
     if not args.no_stack:
         line["stack"] = stack_bench(torch, cfg, args.stack_layers, ms_per_step)
@@ -491,10 +576,17 @@ def main():
         log(f"[bench] {args.stack_layers}-layer decode: {st['ms_per_decode']:.3f} ms, "
             f"{st['beam_tokens_per_s']:.4g} beam-tokens/s; decode steps ~{100 * st['step_share_est']:.0f}%")
 
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, steps, args.cpu_budget)
-        log(f"[bench] CPU oracle: {line['cpu_baseline']['value']:.4g} beam-tokens/s "
-            f"({line['cpu_baseline']['sample']})")
+    if "cpu_baseline" in rec:
+        line["cpu_baseline"] = rec["cpu_baseline"]
+    table = {}
+    if args.table_configs != "none":
+        for idx in (int(x) for x in args.table_configs.split(",")):
+            if idx == args.config:
+                table[f"config{idx}"] = rec
+            else:
+                table[f"config{idx}"], _ = measure_config(torch, onela, inputs, dev, idx, args, headline=False)
+                torch.cuda.empty_cache()
+        line["configs"] = table
     print(json.dumps(line), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Build libonela.so (the HIP library behind include/onela.h) in-tree for gfx950 with hipcc."""
+"""Build libonela.so (the HIP library behind include/onela.h) and libonela_probe.so (the bench's bandwidth
+probe, include/onela_probe.h) in-tree for gfx950 with hipcc."""
 
 import os
 import subprocess
@@ -8,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "lib", "libonela.so")
+PROBE_LIB = os.path.join(PKG, "lib", "libonela_probe.so")
 SOURCES = ["onela_host.cpp", "context.hip", "step_generic.hip", "step_fused.hip", "fullstate.hip",
            "beam_select.hip", "materialize.hip", "prefill_mfma.hip"]
 ARCH = "gfx950"
@@ -22,13 +24,12 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libonela.so; returns its path.  Always recompiles."""
-    os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    tmp = LIB + ".tmp"
+def _compile(sources, out_path, verbose):
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
            "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, "-o", tmp]
-    for src in SOURCES:
+    for src in sources:
         path = os.path.join(CSRC, src)
         cmd += (["-x", "hip", path] if src.endswith(".cpp") else [path])
     if verbose:
@@ -39,8 +40,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libonela.so and libonela_probe.so; returns libonela.so's path.  Always
+    recompiles."""
+    _compile(["hbm_probe.hip"], PROBE_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
