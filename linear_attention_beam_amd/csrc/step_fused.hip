@@ -362,8 +362,10 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
       const uint16_t* kr = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
+        // key piece p of distinct record d holds chunk p ^ (d % 16): the 16 records an MFMA operand read
+        // touches at one chunk sit in different banks
         const int q0 = i * NT + wave * 64, q = q0 + lane;
-        if (q < ndl * 16) dma16(kr + (size_t)pl.ks[i] * kDK + (q & 15) * 8, kd + q0 * 16);
+        if (q < ndl * 16) dma16(kr + (size_t)pl.ks[i] * kDK + (((q & 15) ^ ((q >> 4) & 15)) << 3), kd + q0 * 16);
       }
 #pragma unroll
       for (int i = 0; i < UI; ++i) {
@@ -425,42 +427,15 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's copies into LDS have landed
     __syncthreads();
-    // ---- per beam (16 lanes): k . q, the chain coefficients newest to oldest, the record key and alpha ----
+    // ---- per beam (16 lanes): k . q, the record key and alpha; chain coefficients when read from memory ----
     for (int b = g16; b < nb; b += ngroups) {
       const int beam = pm_t[b];
       const int xo = b * kRow + ((j16 ^ (b & 15)) << 4);
       const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xk + xo);
       const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xq + xo);
       const float kq = row16_sum(dot8_bf16(kx, qx));
-      float cdec = 1.f;
-      if (fast) {
-        // four chain records at a time: their LDS reads and dot products are independent; the decay product is
-        // then applied newest to oldest
-        for (int m = nch - 1; m >= 0; m -= 4) {
-          int d[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) d[j] = li_t[b * L + max(m - j, 0)];
-          u32x4_t K[4];
-          float am[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            K[j] = *reinterpret_cast<const u32x4_t*>(kd + d[j] * kRow + j16 * 16);
-            am[j] = ad[d[j]];
-          }
-          float dk[4], dq[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            dk[j] = row16_sum(dot8_bf16(K[j], kx));
-            dq[j] = row16_sum(dot8_bf16(K[j], qx));
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (m - j >= 0) {
-              if (j16 == 0) coef[b * LS + m - j] = (f32x2_t){cdec * dk[j], cdec * dq[j]};
-              cdec *= am[j];
-            }
-        }
-      } else {
+      if (!fast) {  // step 1 (no chain), or a tile whose distinct records were not staged: newest to oldest
+        float cdec = 1.f;
         const int32_t* crow = a.chain_out + ((size_t)r * a.B_max + beam) * L;
         for (int m = nch - 1; m >= 0; --m) {
           const int sl = crow[m];
@@ -471,15 +446,79 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
           if (j16 == 0) coef[b * LS + m] = (f32x2_t){cdec * dk, cdec * dq};
           cdec *= am;
         }
+        if (j16 == 0) beamA[b] = cdec;
       }
-      if (j16 == 0) {
-        beamA[b] = cdec;
-        beamKq[b] = kq;
-      }
+      if (j16 == 0) beamKq[b] = kq;
       if (rb == 0) {  // the new record's key and alpha
         const unsigned own = (unsigned)(nch * a.B_max + beam);
         *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.rec_k) + (arena + own) * kDK + j16 * 8) = kx;
         if (j16 == 0) a.rec_alpha[arena + own] = al_t[b];
+      }
+    }
+    if (fast) {
+      // Dot products of every staged record key with every beam's k and q on the matrix cores:
+      // [K_D . k | K_D . q] = K_D [k | q]^T, 16 records x 16 beams per output tile, 4 k-steps of 32.  In an output
+      // tile lane l holds beam l % 16 and records 4 (l / 16) .. +3.  Wavefront w takes tiles w, w + NW, ...
+      const int nrt = (ndl + 15) >> 4;
+      const int ntl = nrt * kTiles * 2;
+      constexpr int kMaxT = (kCap / 16) * kTiles * 2 / NW + ((kCap / 16) * kTiles * 2 % NW ? 1 : 0);
+      floatx4_t dacc[kMaxT];
+#pragma unroll
+      for (int i = 0; i < kMaxT; ++i) {
+        const int tl = wave + i * NW;
+        dacc[i] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+        if (tl < ntl) {
+          const int rt = tl / (kTiles * 2), rem = tl - rt * (kTiles * 2), bt = rem >> 1, kqsel = rem & 1;
+          const int d = rt * 16 + col, bb = bt * 16 + col;
+          const unsigned char* xs = kqsel ? xq : xk;
+#pragma unroll
+          for (int k2 = 0; k2 < kKS; ++k2) {
+            const int ch = k2 * 4 + gq;
+            const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kd + d * kRow + ((ch ^ (d & 15)) << 4)));
+            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kRow + ((ch ^ (bb & 15)) << 4)));
+            dacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, kb, dacc[i], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();  // every wavefront is done with the staged keys: their space takes the dot products
+      float* dots = reinterpret_cast<float*>(kd);  // [record][beam][k or q]
+#pragma unroll
+      for (int i = 0; i < kMaxT; ++i) {
+        const int tl = wave + i * NW;
+        if (tl < ntl) {
+          const int rt = tl / (kTiles * 2), rem = tl - rt * (kTiles * 2), bt = rem >> 1, kqsel = rem & 1;
+          const int bb = bt * 16 + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d = rt * 16 + 4 * gq + e;
+            if (d < ndl) dots[(d * NB + bb) * 2 + kqsel] = dacc[i][e];
+          }
+        }
+      }
+      __syncthreads();
+      // per beam, newest to oldest: c_j times the dot products, and the decay product A
+      for (int b = tid; b < nb; b += NT) {
+        const f32x2_t* dd = reinterpret_cast<const f32x2_t*>(dots) + b;
+        float cdec = 1.f;
+        for (int m = nch - 1; m >= 0; m -= 4) {
+          int d[4];
+          f32x2_t v[4];
+          float am[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d[j] = li_t[b * L + max(m - j, 0)];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = dd[d[j] * NB];
+            am[j] = ad[d[j]];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (m - j >= 0) {
+              coef[b * LS + m - j] = (f32x2_t){cdec * v[j].x, cdec * v[j].y};
+              cdec *= am[j];
+            }
+        }
+        beamA[b] = cdec;
       }
     }
     if (nch == 0 && h == 0 && rb == 0) {  // step 1: the first chain rows, and the parents must all be 0
