@@ -246,23 +246,45 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
     int* dlist = reinterpret_cast<int*>(rec + 4);
     unsigned char* li = rec + li_off;
     int base = 0;
-    for (int m = 0; m < L; ++m) {
-      if (m >= nch) {  // own slot, then -1
-        if (live) out[m] = m == nch ? nch * a.B_max + b : -1;
-        continue;
+    for (int m0 = 0; m0 < L; m0 += 8) {
+      // eight chain entries of the parent's row at a time: their loads are independent
+      int vv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[j] = m0 + j < nch ? prow[m0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = m0 + j;
+        if (m >= L) break;
+        if (m >= nch) {  // own slot, then -1
+          if (live) out[m] = m == nch ? nch * a.B_max + b : -1;
+          continue;
+        }
+        const int v = vv[j];
+        if (live) out[m] = v;
+        // first appearances of each record at this position (records at different positions differ: position m
+        // holds slots of step m + 1).  In the sorted order the chains are in lexicographic order, and a record
+        // fixes every entry before it, so the beams holding one record are adjacent: a beam is a first
+        // appearance when its left neighbour holds another record.  Otherwise each lane looks for the first
+        // lane with its value.
+        bool is_first;
+        int place;
+        if (sorted) {
+          const int left = __shfl_up(v, 1, 64);
+          is_first = live && (lane == 0 || left != v);
+          // the first appearances at or before this lane: its own record's is the last of them
+          place = base + __popcll(__ballot(is_first) & ((2ull << lane) - 1ull)) - 1;
+        } else {
+          int o = lane;
+          for (int c = nb - 1; c >= 0; --c)
+            if (__builtin_amdgcn_readlane(v, c) == v) o = c;
+          is_first = live && o == lane;
+          place = base + __popcll(__ballot(is_first) & ((1ull << o) - 1ull));
+        }
+        const unsigned long long first = __ballot(is_first);
+        if (is_first && place < kCap) dlist[place] = v;
+        if (live) li[lane * L + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
+        base += __popcll(first);
       }
-      const int v = prow[m];
-      if (live) out[m] = v;
-      // the first beam of the tile with the same record at this position (records at different positions
-      // differ: position m holds slots of step m + 1)
-      int o = lane;
-      for (int c = nb - 1; c >= 0; --c)
-        if (__builtin_amdgcn_readlane(v, c) == v) o = c;
-      const unsigned long long first = __ballot(live && o == lane);
-      const int place = base + __popcll(first & ((1ull << o) - 1ull));
-      if (live && o == lane && place < kCap) dlist[place] = v;
-      if (live) li[lane * L + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
-      base += __popcll(first);
     }
     if (lane == 0) *reinterpret_cast<int*>(rec) = base;
     if (lane < NB) reinterpret_cast<int*>(rec + perm_off)[lane] = b;
