@@ -91,7 +91,8 @@ def algorithmic_bytes(cfg, chains, parents):
 
 
 def hbm_probe(torch, dev, gib: float = 2.0):
-    """Bandwidth of plain streaming kernels (libonela_probe.so, 16-byte accesses) on this GPU, best of 5 each:
+    """Bandwidth of plain streaming kernels (libonela_probe.so, 16-byte accesses, one element per thread) on this
+    GPU, best of 5 each:
     read-only, the 2:3 read:write mix of the decode step, copy (1:1) and write-only.  Context for the roofline
     fraction (whose peak stays the published 8 TB/s); not part of the timed decode."""
     import ctypes
@@ -105,9 +106,8 @@ def hbm_probe(torch, dev, gib: float = 2.0):
     n = int(gib * (1 << 30)) // 16                      # 16-byte elements per stream
     src = torch.ones(2 * n * 4, dtype=torch.float32, device=dev)
     dst = torch.empty(3 * n * 4, dtype=torch.float32, device=dev)
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    grid = cus * 32  # the best of 4, 8, 16 and 32 workgroups per CU in a sweep of these kernels
-    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    grid = 0  # one element per thread: faster than any grid-stride form of these kernels on this GPU
+    sink = torch.empty(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def best(mode, nbytes):
@@ -130,7 +130,7 @@ def hbm_probe(torch, dev, gib: float = 2.0):
 
     res = {"read_GBs": best(0, 32.0 * n), "mix_2r3w_GBs": best(1, 80.0 * n), "copy_GBs": best(2, 32.0 * n),
            "write_GBs": best(3, 16.0 * n), "bytes_per_stream": 16 * n,
-           "kernel": "onela_probe_stream (16-byte loads/stores, grid-stride, 32 workgroups x 256 threads per CU)"}
+           "kernel": "onela_probe_stream (16-byte loads/stores, one element per thread)"}
     del src, dst, sink
     return res
 

@@ -2,9 +2,11 @@
  * kernel reaches for a given read/write mix on this GPU (context for the decode step's roofline fraction; not
  * part of the decode library).
  *
- * onela_probe_stream enqueues one kernel of `grid` workgroups x 256 threads on `stream`; every access is a
+ * onela_probe_stream enqueues one kernel of 256-thread workgroups on `stream`: with grid = 0, one element per
+ * thread (ceil(n / 256) workgroups); with grid > 0, that many workgroups in a grid-stride loop.  Every access is a
  * 16-byte vector load or store and n counts 16-byte elements:
- *   mode 0 read    src holds 2n elements, all read; sink (grid x 256 floats) receives per-thread sums
+ *   mode 0 read    src holds 2n elements, all read; with grid > 0 sink (grid x 256 floats) receives per-thread
+ *                  sums (with grid = 0 sink must still be a valid device pointer; it is almost never written)
  *   mode 1 mix     src holds 2n elements, all read; dst holds 3n elements, all written (2 : 3 bytes)
  *   mode 2 copy    src and dst hold n elements; dst = src
  *   mode 3 write   dst holds n elements, all written with a constant

@@ -19,6 +19,6 @@ def test_probe_exports_and_argument_checks():
     fn.restype = ctypes.c_int
     assert fn(None, None, 16, 7, None, 1, None) == 1      # unknown mode
     assert fn(None, None, 0, 2, None, 1, None) == 1       # empty
-    assert fn(None, None, 16, 2, None, 0, None) == 1      # no workgroups
+    assert fn(None, None, 16, 2, None, -1, None) == 1     # negative grid
     assert fn(None, None, 16, 1, None, 1, None) == 1      # the mix needs both buffers
     assert fn(None, None, 16, 0, None, 1, None) == 1      # read needs src and the sink
