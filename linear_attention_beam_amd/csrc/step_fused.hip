@@ -8,6 +8,8 @@
 //     previous step's order, which keeps the whole chains in lexicographic order).  Beams with common
 //     ancestors then share tiles, so a tile touches few distinct records and neighbouring tiles share the rest.
 //     The order only decides which workgroup computes which beam: every output lands at its beam's place.
+//     The sort places siblings the same way in every run, so the tiles, and with them which tiles read
+//     their records from memory instead of LDS (a different summation order), repeat exactly.
 //   * One plan per tile of NB consecutive beams in that order, shared by every head (slots are the same for
 //     all heads): the beams, the distinct ancestor slots (chain position by chain position, in order of first
 //     appearance) and, for each beam and chain position, the place of its record in that list.
@@ -187,10 +189,12 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
                                                              int plan_bytes, int perm_off, int li_off,
                                                              int* __restrict__ rank) {
   static_assert(NB <= 64, "one lane per beam of a tile");
+  constexpr int kParts = 8;  // parts of the beam range, each counted and placed by one wavefront
   __shared__ int s_par[kSort];
   __shared__ int s_key[kSort];
   __shared__ int s_perm[kSort];
-  __shared__ int s_cnt[kSort + 1];
+  __shared__ int s_tot[kSort];
+  __shared__ int s_cnt[kParts][kSort];
   const int L = a.L_max, n = a.n, t = a.t, nch = t - 1;
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
@@ -206,28 +210,51 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
     return p;
   };
   if (sorted) {
-    for (int k = tid; k <= a.b_prev; k += nt) s_cnt[k] = 0;
+    // A counting sort whose result is the same in every run: the beam range is cut into kParts parts, each
+    // counted and placed by one wavefront with counters of its own, so no two wavefronts race on a counter.
+    // Siblings (beams of one key) are placed part by part, within a part as its wavefront's atomics return.
+    const int K = a.b_prev, C = (n + kParts - 1) / kParts;
+    const int p0 = wave * C, p1 = min(n, p0 + C);
+    for (int i = tid; i < kParts * K; i += nt) s_cnt[i / K][i % K] = 0;
     __syncthreads();
-    for (int b = tid; b < n; b += nt) {
-      const int p = parent_of(b);
-      s_par[b] = p;
-      // the parent's place in the previous step's order (step 1 has a single beam)
-      const int key = nch == 1 ? p : rank[(size_t)r * a.B_max + p];
-      s_key[b] = key;
-      atomicAdd(&s_cnt[key + 1], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive offsets of the keys
-      int carry = 0;
-      for (int k0 = 0; k0 <= a.b_prev; k0 += 64) {
-        const int k = k0 + lane;
-        const int x = wave_scan(k <= a.b_prev ? s_cnt[k] : 0);
-        if (k <= a.b_prev) s_cnt[k] = carry + x;
-        carry += __shfl(x, 63, 64);
+    if (wave < kParts) {
+      for (int b = p0 + lane; b < p1; b += 64) {
+        const int p = parent_of(b);
+        s_par[b] = p;
+        // the parent's place in the previous step's order (step 1 has a single beam)
+        const int key = nch == 1 ? p : rank[(size_t)r * a.B_max + p];
+        s_key[b] = key;
+        atomicAdd(&s_cnt[wave][key], 1);
       }
     }
     __syncthreads();
-    for (int b = tid; b < n; b += nt) s_perm[atomicAdd(&s_cnt[s_key[b]], 1)] = b;
+    for (int k = tid; k < K; k += nt) {  // per key: each part's offset within the key's run, and its length
+      int run = 0;
+      for (int g = 0; g < kParts; ++g) {
+        const int c = s_cnt[g][k];
+        s_cnt[g][k] = run;
+        run += c;
+      }
+      s_tot[k] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive offsets of the keys' runs
+      int carry = 0;
+      for (int k0 = 0; k0 < K; k0 += 64) {
+        const int k = k0 + lane;
+        const int x = k < K ? s_tot[k] : 0;
+        const int inc = wave_scan(x);
+        if (k < K) s_tot[k] = carry + inc - x;
+        carry += __shfl(inc, 63, 64);
+      }
+    }
+    __syncthreads();
+    if (wave < kParts) {
+      for (int b = p0 + lane; b < p1; b += 64) {
+        const int k = s_key[b];
+        s_perm[s_tot[k] + atomicAdd(&s_cnt[wave][k], 1)] = b;
+      }
+    }
     __syncthreads();
     for (int pos = tid; pos < n; pos += nt) rank[(size_t)r * a.B_max + s_perm[pos]] = pos;
   } else {

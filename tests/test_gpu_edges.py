@@ -113,6 +113,25 @@ def test_deterministic():
     assert torch.equal(a.view["rec_u"], b.view["rec_u"])
 
 
+@pytest.mark.parametrize("ci", [3, 4])
+def test_deterministic_full_size(ci):
+    """Two decodes of a full-size workload agree bit for bit: the processing order places siblings the same way
+    in every run, so the tiles, and which of them read their records from memory instead of LDS, repeat."""
+    cfg = inputs.config(ci)
+    gu.log(f"determinism at full size: {cfg.name}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = inputs.direct_sctx(cfg)
+    a = gu.GpuRun(cfg, steps, sctx=sctx)
+    outs_a = [o.clone() for o in a.outs]
+    u_a = a.view["rec_u"].clone()
+    a.ctx.close()
+    del a
+    b = gu.GpuRun(cfg, steps, sctx=sctx)
+    for t in range(cfg.L):
+        assert torch.equal(outs_a[t].view(torch.int32), b.outs[t].view(torch.int32)), f"step {t + 1}"
+    assert torch.equal(u_a.view(torch.int32), b.view["rec_u"].view(torch.int32))
+
+
 @pytest.mark.parametrize("mode", ["replay", "fullstate"])
 def test_parent_out_of_range_is_flagged(mode):
     cfg = inputs.config(2, R=2, H=2, B=32, L=3)
