@@ -44,8 +44,12 @@ constexpr int kCap = 64;        // distinct ancestor records of a tile staged in
 constexpr int kSort = 2048;     // beams per request the plan kernel sorts (more: they keep their own order)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+// Bytes per beam of the record places (one per chain position): a multiple of 8, so that the replay reads a
+// beam's places eight at a time.
+__host__ __device__ inline int li_stride(int L) { return (L + 7) & ~7; }
 
 // Plan record of one (request, tile), in bytes: nd, the distinct slots (up to kCap), the NB beams (padded with
 // the last beam), then one byte per (beam, chain position): the place of its record in the distinct list.
@@ -56,7 +60,7 @@ __host__ __device__ inline PlanLayout plan_layout(int NB, int L) {
   PlanLayout p;
   p.perm = align16(4 + 4 * kCap);
   p.li = p.perm + NB * 4;
-  p.bytes = p.li + align16(NB * L);
+  p.bytes = p.li + align16(NB * li_stride(L));
   return p;
 }
 
@@ -64,7 +68,9 @@ __host__ __device__ inline PlanLayout plan_layout(int NB, int L) {
 struct FusedLds {
   int xk, xq, xv, al, be, pm, li, kd, ud, ad, coef, beamA, beamKq, total;
 };
-__host__ __device__ inline int coef_stride(int L) { return L | 1; }  // odd: 16 beams in distinct banks
+// Coefficients per beam: room for the chain rounded up to four positions (those past the chain hold zeros),
+// odd so that 16 beams fall in distinct banks.
+__host__ __device__ inline int coef_stride(int L) { return ((L + 3) & ~3) | 1; }
 __host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB) {
   FusedLds y;
   int o = 0;
@@ -74,7 +80,7 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB) {
   y.al = o;  o += align16(NB * 4);
   y.be = o;  o += align16(NB * 4);
   y.pm = o;  o += align16(NB * 4);         // the tile's beams
-  y.li = o;  o += align16(NB * L);         // place of each chain record in the distinct list
+  y.li = o;  o += align16(NB * li_stride(L));  // place of each chain record in the distinct list
   y.kd = o;  o += kCap * kRow;             // keys of the distinct records
   y.ud = o;  o += kCap * RB * 4;           // their u rows of this row block, 16-byte pieces swizzled by record
   y.ad = o;  o += align16(kCap * 4);       // their alphas at this head
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
         }
         const unsigned long long first = __ballot(is_first);
         if (is_first && place < kCap) dlist[place] = v;
-        if (live) li[lane * L + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
+        if (live) li[lane * li_stride(L) + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
         base += __popcll(first);
       }
     }
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
   constexpr int kTiles = NB / 16;
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v, t = a.t, nch = t - 1;
   const FusedLds lay = fused_layout(NB, L, RB);
-  const int LS = coef_stride(L);
+  const int LS = coef_stride(L), LIS = li_stride(L);
   constexpr int ngroups = NT / 16;
   const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs (elements)
   unsigned char* xk = lds + lay.xk;
@@ -426,8 +432,8 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
       if (wave == 0 && lane < ndl) dma4(a.rec_alpha + arena + pl.as, lds + lay.ad);
       if (nch > 0) {
         if (wave == 0 && lane < NB) dma4(prec + perm_off + lane * 4, lds + lay.pm);
-        for (int q0 = wave * 64; q0 < NB * L / 4; q0 += NT)
-          if (q0 + lane < NB * L / 4 && ndl > 0) dma4(prec + li_off + (q0 + lane) * 4, lds + lay.li + q0 * 4);
+        for (int q0 = wave * 64; q0 < NB * LIS / 4; q0 += NT)
+          if (q0 + lane < NB * LIS / 4 && ndl > 0) dma4(prec + li_off + (q0 + lane) * 4, lds + lay.li + q0 * 4);
       }
     }
     // ---- the k, q and v rows; alpha and beta ----
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
           f32x2_t v[4];
           float am[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) d[j] = li_t[b * L + max(m - j, 0)];
+          for (int j = 0; j < 4; ++j) d[j] = li_t[b * LIS + max(m - j, 0)];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             v[j] = dd[d[j] * NB];
@@ -567,6 +573,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
               cdec *= am[j];
             }
         }
+        for (int m = nch; m < ((nch + 3) & ~3); ++m) coef[b * LS + m] = (f32x2_t){0.f, 0.f};
         beamA[b] = cdec;
       }
     }
@@ -604,28 +611,34 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
       }
       floatx4_t P = (floatx4_t){0.f, 0.f, 0.f, 0.f}, Q = (floatx4_t){0.f, 0.f, 0.f, 0.f};
       if (fast) {
-        // four chain records at a time, their LDS reads issued together
-        for (int m0 = 0; m0 < nch; m0 += 4) {
-          int d[4];
-          f32x2_t cf[4];
+        // the places of eight chain positions in one read, then four records at a time, their coefficient and
+        // u reads issued together
+        for (int m8 = 0; m8 < nch; m8 += 8) {
+          const u32x2_t lw = *reinterpret_cast<const u32x2_t*>(li_t + bc * LIS + m8);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int mm = min(m0 + j, nch - 1);
-            d[j] = li_t[bc * L + mm];
-            cf[j] = coef[bc * LS + mm];
-            if (m0 + j >= nch) cf[j] = (f32x2_t){0.f, 0.f};
-          }
-          f32x4_t uu[4];
+          for (int h4 = 0; h4 < 2; ++h4) {
+            const int m0 = m8 + 4 * h4;
+            if (m0 >= nch) break;
+            const unsigned word = h4 ? lw.y : lw.x;
+            int d[4];
+            f32x2_t cf[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            uu[j] = *reinterpret_cast<const f32x4_t*>(ud + d[j] * (RB * 4) + (((dvl >> 2) ^ (d[j] & (UP - 1))) << 4));
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              P[e] += cf[j].x * uu[j][e];
-              Q[e] += cf[j].y * uu[j][e];
+            for (int j = 0; j < 4; ++j) {  // past the chain: record 0, with the zero coefficient written there
+              d[j] = m0 + j < nch ? (int)((word >> (8 * j)) & 255u) : 0;
+              cf[j] = coef[bc * LS + m0 + j];
             }
+            f32x4_t uu[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              uu[j] = *reinterpret_cast<const f32x4_t*>(ud + d[j] * (RB * 4) + (((dvl >> 2) ^ (d[j] & (UP - 1))) << 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                P[e] += cf[j].x * uu[j][e];
+                Q[e] += cf[j].y * uu[j][e];
+              }
+          }
         }
       } else {
         const int32_t* crow = a.chain_out + ((size_t)r * a.B_max + pm_t[bc]) * L;

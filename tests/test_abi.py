@@ -47,8 +47,10 @@ def expected_bytes(c):
     total = 256 + up(R * H * dk * dv * 4) + up(R * H * dk * dv * 4 if fused else 0) + up(L * R * B * L * 4)
     a16 = lambda x: (x + 15) // 16 * 16  # noqa: E731
     # per (request, tile of 16 or 32 beams) plans: nd and up to 64 distinct slots, the tile's beams, one byte per
-    # (beam, chain position); the larger of the two tile sizes, then the processing order rank[R][B]
-    plan = up(max(R * (-(-B // nb)) * (a16(4 + 4 * 64) + 4 * nb + a16(nb * L)) for nb in (16, 32))) + R * B * 4
+    # (beam, chain position) with the positions of a beam padded to a multiple of 8; the larger of the two tile
+    # sizes, then the processing order rank[R][B]
+    L8 = -(-L // 8) * 8
+    plan = up(max(R * (-(-B // nb)) * (a16(4 + 4 * 64) + 4 * nb + a16(nb * L8)) for nb in (16, 32))) + R * B * 4
     total += up(plan if fused else 0)
     if c.mode == onela.ONELA_MODE_REPLAY:
         slots = B * L
