@@ -19,7 +19,9 @@ Prints one JSON line.  Extra objects:
   materialize   the materializing-replay path (each beam's dense parent state rebuilt every step) on the same
                 inputs
   hbm_probe     read-only, 2:3 read:write mix, copy and write-only bandwidth of plain streaming kernels
-                (libonela_probe.so) on the same GPU (context for the fraction)
+                (libonela_probe.so) on the same GPU, and the first decode step's traffic (the same rows read
+                and written at the workload's shape) from a plain kernel without the arithmetic (context for
+                the fraction)
   beam_select   the beam selection that produces each step's parents (top B of B x 256 candidate scores per
                 request), timed on its own with HIP events; not part of the decode step above
   prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the dense
@@ -90,7 +92,46 @@ def algorithmic_bytes(cfg, chains, parents):
     return out
 
 
-def hbm_probe(torch, dev, gib: float = 2.0):
+def step_traffic_probe(torch, dev, lib, cfg, reps: int = 5):
+    """The first decode step's traffic without its arithmetic (onela_probe_step_traffic: the same k, q, v, alpha,
+    beta and S_ctx reads and o, u, key and alpha writes, one plain workgroup per (request, head, 32-beam tile)) at
+    the workload's shape, best of ``reps``: the rate this access pattern reaches on this GPU."""
+    import ctypes
+    R, B, H, dv, slots = cfg.R, cfg.B, cfg.H, cfg.d_v, cfg.B * cfg.L
+    fn = lib.onela_probe_step_traffic
+    fn.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    bf = torch.bfloat16
+    k = torch.ones((R, B, H, 128), dtype=bf, device=dev)
+    q = torch.ones((R, B, H, 128), dtype=bf, device=dev)
+    v = torch.ones((R, B, H, dv), dtype=bf, device=dev)
+    ab = torch.ones((2, R, B, H), dtype=torch.float32, device=dev)
+    sctx = torch.ones((R * H, 128, dv), dtype=torch.float32, device=dev)
+    o = torch.empty((R, B, H, dv), dtype=torch.float32, device=dev)
+    u = torch.empty((R * H, slots, dv), dtype=torch.float32, device=dev)
+    rk = torch.empty((R * H, slots, 128), dtype=bf, device=dev)
+    ra = torch.empty((R * H, slots), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = [t.data_ptr() for t in (k, q, v, ab[0], ab[1], sctx, o, u, rk, ra)] + [R, B, H, dv, slots,
+                                                                                    stream.cuda_stream]
+    nbytes = R * B * H * (2 * 256 + 2 * dv + 8 + 4 * dv + 4 * dv + 256 + 4) + R * H * 128 * dv * 4
+    if fn(*args) != 0:
+        raise RuntimeError("onela_probe_step_traffic failed")
+    torch.cuda.synchronize()
+    best_us = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(*args)
+        b.record(stream)
+        torch.cuda.synchronize()
+        best_us = min(best_us, a.elapsed_time(b) * 1e3)
+    del k, q, v, ab, sctx, o, u, rk, ra
+    return {"workload": cfg.name, "bytes": nbytes, "us": best_us, "GBs": nbytes / (best_us * 1e-6) / 1e9,
+            "kernel": "onela_probe_step_traffic (one 256-thread workgroup per request, head and 32-beam tile)"}
+
+
+def hbm_probe(torch, dev, cfg=None, gib: float = 2.0):
     """Bandwidth of plain streaming kernels (libonela_probe.so, 16-byte accesses, one element per thread) on this
     GPU, best of 5 each:
     read-only, the 2:3 read:write mix of the decode step, copy (1:1) and write-only.  Context for the roofline
@@ -132,6 +173,8 @@ def hbm_probe(torch, dev, gib: float = 2.0):
            "write_GBs": best(3, 16.0 * n), "bytes_per_stream": 16 * n,
            "kernel": "onela_probe_stream (16-byte loads/stores, one element per thread)"}
     del src, dst, sink
+    if cfg is not None:
+        res["step1_traffic"] = step_traffic_probe(torch, dev, lib, cfg)
     return res
 
 
@@ -530,9 +573,14 @@ def main():
         line["prefill"] = extra["prefill"]
     if "fullstate" in extra:
         line["fullstate"] = extra["fullstate"]
-    line["hbm_probe"] = hbm_probe(torch, dev)
+    line["hbm_probe"] = hbm_probe(torch, dev, cfg)
+    st1 = line["hbm_probe"]["step1_traffic"]
+    # step 1 of the timed decodes against the same traffic from a plain kernel
+    st1["decode_step1_us"] = rec["step_us_by_decode_step"][0]
+    st1["probe_over_decode_step1"] = st1["us"] / rec["step_us_by_decode_step"][0]
     log(f"[bench] probes: read {line['hbm_probe']['read_GBs']:.0f}, 2:3 mix {line['hbm_probe']['mix_2r3w_GBs']:.0f}, "
-        f"copy {line['hbm_probe']['copy_GBs']:.0f}, write {line['hbm_probe']['write_GBs']:.0f} GB/s")
+        f"copy {line['hbm_probe']['copy_GBs']:.0f}, write {line['hbm_probe']['write_GBs']:.0f} GB/s; "
+        f"step-1 traffic of {st1['workload']}: {st1['GBs']:.0f} GB/s ({st1['us']:.1f} us)")
     if not args.no_select:
         line["beam_select"] = select_bench(torch, dev, cfg, with_cpu=not args.no_cpu_baseline)
         log(f"[bench] beam selection {line['beam_select']['shape']}: {line['beam_select']['us_per_call']:.1f} us/call")
