@@ -40,6 +40,7 @@ constexpr int kChunk = kThreads * kPerThread;  // keys per workgroup
 constexpr int kMaxBeams = 2048;
 constexpr int kHistCopies = 8;                 // lanes l with l % 8 == c share histogram copy c
 constexpr int kHistStride = 260;               // ints per copy: the copies of one digit sit in different banks
+constexpr int kBucket = 64;                    // a threshold bucket this small is finished by one wavefront
 
 __device__ __forceinline__ uint32_t score_order(float x) {
   uint32_t u = __float_as_uint(x);
@@ -56,7 +57,8 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t f) {
 struct alignas(16) SelLds {
   int hist[kHistCopies][kHistStride];
   unsigned long long wmin[kThreads / 64], wmax[kThreads / 64];
-  int digit, rank, count, n_out;
+  uint64_t bucket[kBucket], thr;
+  int digit, rank, count, n_out, n_bucket;
   uint64_t best[kMaxBeams];
   uint64_t sorted[kMaxBeams];
 };
@@ -95,10 +97,39 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, i
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// The rank-th largest of the cnt (<= kBucket) keys k with (k & mask) == prefix: they are gathered in LDS, and
+// each lane of one wavefront counts the gathered keys above its own.  Every thread must call it.
+__device__ __forceinline__ uint64_t bucket_pick(const uint64_t (&key)[kPerThread], uint64_t prefix, uint64_t mask,
+                                                int cnt, int rank, SelLds& sh) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool in = (key[e] & mask) == prefix;  // the keys the last histogram pass counted in the bucket
+    const uint64_t take = __ballot(in);
+    if (take) {  // one atomic per wavefront
+      const int first = __ffsll((long long)take) - 1;
+      int base = 0;
+      if (lane == first) base = atomicAdd(&sh.n_bucket, __popcll(take));
+      base = __shfl(base, first, 64);
+      if (in) sh.bucket[base + __popcll(take & ((1ull << lane) - 1))] = key[e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const uint64_t x = lane < cnt ? sh.bucket[lane] : 0ull;
+    int above = 0;
+    for (int j = 0; j < cnt; ++j) above += sh.bucket[j] > x;
+    if (lane < cnt && above == rank - 1) sh.thr = x;  // keys are unique: exactly one lane
+  }
+  __syncthreads();
+  return sh.thr;
+}
+
 // Smallest key T such that exactly K of the workgroup's unique keys are >= T (requires 1 <= K <= the number
 // of nonzero keys).  Every thread must call it.  Digits start at the highest bit where the smallest and the
 // largest real key differ: the bits above are common to all of them and would only cost passes that split
-// nothing.
+// nothing.  Once the bucket that holds T has at most kBucket keys, T is picked from them directly: at
+// 32 x 512 x 256 candidates every chunk then needs at most two histogram passes (up to seven before).
 __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerThread], int K, SelLds& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, copy = lane & (kHistCopies - 1);
   unsigned long long lo = ~0ull, hi = 0ull;
@@ -117,6 +148,7 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerTh
     sh.wmax[wave] = hi;
   }
   for (int i = tid; i < kHistCopies * kHistStride; i += kThreads) (&sh.hist[0][0])[i] = 0;
+  if (tid == 0) sh.n_bucket = 0;
   __syncthreads();
   lo = ~0ull;
   hi = 0ull;
@@ -179,6 +211,7 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerTh
     prefix |= (uint64_t)d << shift;
     mask |= (uint64_t)((1u << w) - 1u) << shift;
     if (cnt == rank || shift == 0) break;  // the whole bucket is taken: exactly K keys are >= prefix
+    if (cnt <= kBucket) return bucket_pick(key, prefix, mask, cnt, rank, sh);
     top = shift - 1;
   }
   return prefix;
