@@ -200,12 +200,13 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
   __shared__ int s_key[kSort];
   __shared__ int s_perm[kSort];
   __shared__ int s_tot[kSort];
+  __shared__ int s_wsum[kSort / 64];
   __shared__ int s_cnt[kParts][kSort];
   const int L = a.L_max, n = a.n, t = a.t, nch = t - 1;
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
   const int ntile = (n + NB - 1) / NB;
-  const bool sorted = n <= kSort && a.b_prev <= kSort;
+  const bool sorted = n <= kSort && a.b_prev <= kSort && 2 * nt >= kSort;
   const int* parent = a.parent + (size_t)r * n;
   auto parent_of = [&](int b) {  // range-checked: a bad index raises the sticky flag and becomes 0
     int p = parent[b];
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
     // Siblings (beams of one key) are placed part by part, within a part as its wavefront's atomics return.
     const int K = a.b_prev, C = (n + kParts - 1) / kParts;
     const int p0 = wave * C, p1 = min(n, p0 + C);
-    for (int i = tid; i < kParts * K; i += nt) s_cnt[i / K][i % K] = 0;
+    for (int g = 0; g < kParts; ++g)
+      for (int k = tid; k < K; k += nt) s_cnt[g][k] = 0;
     __syncthreads();
     if (wave < kParts) {
       for (int b = p0 + lane; b < p1; b += 64) {
@@ -234,24 +236,34 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
       }
     }
     __syncthreads();
-    for (int k = tid; k < K; k += nt) {  // per key: each part's offset within the key's run, and its length
-      int run = 0;
-      for (int g = 0; g < kParts; ++g) {
-        const int c = s_cnt[g][k];
-        s_cnt[g][k] = run;
-        run += c;
+    {
+      // Per key k (thread k, and k + nt): each part's offset within the key's run, and the run's length.  Then
+      // the runs' exclusive offsets: a scan within each wavefront, plus the totals of the wavefronts before it.
+      int run[2], inc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = h * nt + tid;
+        run[h] = 0;
+        if (k < K) {
+          int c[kParts];
+#pragma unroll
+          for (int g = 0; g < kParts; ++g) c[g] = s_cnt[g][k];
+#pragma unroll
+          for (int g = 0; g < kParts; ++g) {
+            s_cnt[g][k] = run[h];
+            run[h] += c[g];
+          }
+        }
+        inc[h] = wave_scan(run[h]);
+        if (lane == 63) s_wsum[h * nwaves + wave] = inc[h];
       }
-      s_tot[k] = run;
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive offsets of the keys' runs
-      int carry = 0;
-      for (int k0 = 0; k0 < K; k0 += 64) {
-        const int k = k0 + lane;
-        const int x = k < K ? s_tot[k] : 0;
-        const int inc = wave_scan(x);
-        if (k < K) s_tot[k] = carry + inc - x;
-        carry += __shfl(inc, 63, 64);
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = h * nt + tid;
+        // the totals of the wavefronts before this one: one per lane, summed across the wavefront
+        const int before = __shfl(wave_scan(lane < h * nwaves + wave ? s_wsum[lane] : 0), 63, 64);
+        if (k < K) s_tot[k] = before + inc[h] - run[h];
       }
     }
     __syncthreads();
@@ -284,6 +296,7 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
       int vv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) vv[j] = m0 + j < nch ? prow[m0 + j] : -1;
+      unsigned lib[2] = {0u, 0u};  // the eight places, stored at once (one byte each)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int m = m0 + j;
@@ -315,9 +328,10 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
         }
         const unsigned long long first = __ballot(is_first);
         if (is_first && place < kCap) dlist[place] = v;
-        if (live) li[lane * li_stride(L) + m] = (unsigned char)place;  // unused by the fused kernel unless nd <= kCap
+        lib[j >> 2] |= (unsigned)(place & 255) << (8 * (j & 3));  // unused by the fused kernel unless nd <= kCap
         base += __popcll(first);
       }
+      if (live && m0 < nch) *reinterpret_cast<u32x2_t*>(li + lane * li_stride(L) + m0) = (u32x2_t){lib[0], lib[1]};
     }
     if (lane == 0) *reinterpret_cast<int*>(rec) = base;
     if (lane < NB) reinterpret_cast<int*>(rec + perm_off)[lane] = b;
