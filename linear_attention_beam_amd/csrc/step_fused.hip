@@ -201,12 +201,13 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
   __shared__ int s_perm[kSort];
   __shared__ int s_tot[kSort];
   __shared__ int s_wsum[kSort / 64];
-  __shared__ int s_cnt[kParts][kSort];
+  // per part, two 16-bit counters per word: key k in half k & 1 of word k >> 1 (no count reaches 2^16)
+  __shared__ unsigned s_cnt[kParts][kSort / 2];
   const int L = a.L_max, n = a.n, t = a.t, nch = t - 1;
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
   const int ntile = (n + NB - 1) / NB;
-  const bool sorted = n <= kSort && a.b_prev <= kSort && 2 * nt >= kSort;
+  const bool sorted = n <= kSort && a.b_prev <= kSort && nt >= kSort / 2;
   const int* parent = a.parent + (size_t)r * n;
   auto parent_of = [&](int b) {  // range-checked: a bad index raises the sticky flag and becomes 0
     int p = parent[b];
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
     const int K = a.b_prev, C = (n + kParts - 1) / kParts;
     const int p0 = wave * C, p1 = min(n, p0 + C);
     for (int g = 0; g < kParts; ++g)
-      for (int k = tid; k < K; k += nt) s_cnt[g][k] = 0;
+      for (int w = tid; w < (K + 1) / 2; w += nt) s_cnt[g][w] = 0u;
     __syncthreads();
     if (wave < kParts) {
       for (int b = p0 + lane; b < p1; b += 64) {
@@ -232,45 +233,41 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
         // the parent's place in the previous step's order (step 1 has a single beam)
         const int key = nch == 1 ? p : rank[(size_t)r * a.B_max + p];
         s_key[b] = key;
-        atomicAdd(&s_cnt[wave][key], 1);
+        atomicAdd(&s_cnt[wave][key >> 1], 1u << (16 * (key & 1)));
       }
     }
     __syncthreads();
     {
-      // Per key k (thread k, and k + nt): each part's offset within the key's run, and the run's length.  Then
-      // the runs' exclusive offsets: a scan within each wavefront, plus the totals of the wavefronts before it.
-      int run[2], inc[2];
+      // Keys 2 tid and 2 tid + 1: each part's offset within the key's run, and the runs' lengths.  Then the
+      // runs' exclusive offsets: a scan within each wavefront, plus the totals of the wavefronts before it.
+      const int k0 = 2 * tid;
+      int run0 = 0, run1 = 0;
+      if (k0 < K) {
+        unsigned c[kParts];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = h * nt + tid;
-        run[h] = 0;
-        if (k < K) {
-          int c[kParts];
+        for (int g = 0; g < kParts; ++g) c[g] = s_cnt[g][tid];
 #pragma unroll
-          for (int g = 0; g < kParts; ++g) c[g] = s_cnt[g][k];
-#pragma unroll
-          for (int g = 0; g < kParts; ++g) {
-            s_cnt[g][k] = run[h];
-            run[h] += c[g];
-          }
+        for (int g = 0; g < kParts; ++g) {
+          s_cnt[g][tid] = (unsigned)run0 | ((unsigned)run1 << 16);
+          run0 += (int)(c[g] & 0xFFFFu);
+          run1 += (int)(c[g] >> 16);
         }
-        inc[h] = wave_scan(run[h]);
-        if (lane == 63) s_wsum[h * nwaves + wave] = inc[h];
       }
+      const int pair = run0 + run1, inc = wave_scan(pair);
+      if (lane == 63) s_wsum[wave] = inc;
       __syncthreads();
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = h * nt + tid;
-        // the totals of the wavefronts before this one: one per lane, summed across the wavefront
-        const int before = __shfl(wave_scan(lane < h * nwaves + wave ? s_wsum[lane] : 0), 63, 64);
-        if (k < K) s_tot[k] = before + inc[h] - run[h];
-      }
+      // the totals of the wavefronts before this one: one per lane, summed across the wavefront
+      const int before = __shfl(wave_scan(lane < wave ? s_wsum[lane] : 0), 63, 64) + inc - pair;
+      if (k0 < K) s_tot[k0] = before;
+      if (k0 + 1 < K) s_tot[k0 + 1] = before + run0;
     }
     __syncthreads();
     if (wave < kParts) {
       for (int b = p0 + lane; b < p1; b += 64) {
         const int k = s_key[b];
-        s_perm[s_tot[k] + atomicAdd(&s_cnt[wave][k], 1)] = b;
+        const unsigned sh = 16u * (unsigned)(k & 1);
+        const unsigned old = atomicAdd(&s_cnt[wave][k >> 1], 1u << sh);
+        s_perm[s_tot[k] + (int)((old >> sh) & 0xFFFFu)] = b;
       }
     }
     __syncthreads();
