@@ -282,15 +282,22 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
     runs[run * 64 + lane] = x;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nrun * 64; i += kThreads) {
+  // Each survivor's rank is the sum of two halves, each counted by its own thread: its place in its own run plus
+  // the searches of the first half of the runs, and the searches of the second half.  The halves go to the
+  // histogram space when they fit, else to the survivors' space (read back before the survivors are placed).
+  const int half = (nrun + 1) >> 1, nsurv = nrun * 64;
+  const bool in_hist = 2 * nsurv <= kHistCopies * kHistStride;
+  int* part = in_hist ? &sh.hist[0][0] : reinterpret_cast<int*>(sh.best);
+  for (int it = threadIdx.x; it < 2 * nsurv; it += kThreads) {
+    const int h = it >= nsurv, i = it - h * nsurv;
     const uint64_t x = runs[i];
-    const int own = i >> 6;
-    int rank = i & 63;
-    for (int b0 = 0; b0 < nrun; b0 += 8) {  // 8 independent searches in flight
+    const int own = i >> 6, bl = h * half, bh = min(nrun, bl + half);
+    int rank = h ? 0 : (i & 63);
+    for (int b0 = bl; b0 < bh; b0 += 8) {  // 8 independent searches in flight
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int b = b0 + u;
-        if (b < nrun && b != own) {
+        if (b < bh && b != own) {
           const uint64_t* rb = runs + b * 64;
           int pos = 0;
 #pragma unroll
@@ -301,7 +308,27 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
         }
       }
     }
-    if (x != 0ull) sh.best[rank] = x;  // key 0 is padding
+    part[it] = rank;
+  }
+  __syncthreads();
+  if (in_hist) {
+    for (int i = threadIdx.x; i < nsurv; i += kThreads) {
+      const uint64_t x = runs[i];
+      if (x != 0ull) sh.best[part[i] + part[nsurv + i]] = x;  // key 0 is padding
+    }
+  } else {
+    int rk[kMaxBeams / kThreads];
+#pragma unroll
+    for (int e = 0; e < kMaxBeams / kThreads; ++e) {
+      const int i = e * kThreads + threadIdx.x;
+      rk[e] = i < nsurv ? part[i] + part[nsurv + i] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kMaxBeams / kThreads; ++e) {
+      const int i = e * kThreads + threadIdx.x;
+      if (i < nsurv && runs[i] != 0ull) sh.best[rk[e]] = runs[i];
+    }
   }
   __syncthreads();
   // the score is recomputed from its inputs (the same float32 addition), so its sign survives
