@@ -58,7 +58,13 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(FUSED_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the step kernels' source code, comments and blank lines left out (the code the counters ran)."""
+    lines = []
+    for line in open(FUSED_SRC, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def algorithmic_bytes(cfg, chains, parents):

@@ -21,14 +21,16 @@
 //   * one round trip brings everything into LDS: the beams' k, q and v rows (16-byte loads through registers),
 //     and, copied straight into LDS (global_load_lds), the keys, alphas and u rows of the tile's distinct
 //     ancestor records, the beams and the plan places.  The plan itself was loaded during the previous tile;
-//   * 16 lanes per beam walk its chain newest to oldest, taking the dot products of the record keys with k and
-//     q, scaled by the decay product c_j of the alphas after record j (four records at a time);
+//   * the dot products of every staged record key with every beam's k and q on the matrix cores (16 records x
+//     16 beams per output tile); then one thread per beam walks its chain newest to oldest, scaling them by the
+//     decay product c_j of the alphas after record j;
 //   * per 16 beams, v_mfma_f32_16x16x32_bf16 forms [P_k | P_q]^T = S_rows [k | q], high then low half into one
 //     float32 accumulator; in the accumulator lane l holds beam l % 16 and d_v rows 4 (l / 16) .. +3 of the
 //     wavefront's 16 rows, so the replay works per beam on 16-byte pieces of u, and u and o leave as float4:
 //       p = A P_k + sum_j c_j (K_j . k) U_j,   u = beta (v - alpha p),
 //       o = alpha (A P_q + sum_j c_j (K_j . q) U_j) + (k . q) u,        A = prod_j alpha_j.
-//   A tile whose distinct records do not fit in LDS reads them from memory instead (same arithmetic).
+//   A tile whose distinct records do not fit in LDS reads them from memory instead: 16 lanes per beam take the
+//   key dot products (a different summation order from the matrix cores') and the replay reads u from memory.
 #include <algorithm>
 
 #include "device_common.h"
