@@ -11,7 +11,8 @@
 // Selection without sorting everything: a workgroup of 1024 threads holds up to 8192 keys in registers
 // (8 per thread) and an MSB-first radix select finds the smallest key T such that exactly K keys are >= T
 // (8-bit digits from the highest bit where the keys differ, one LDS histogram per pass; it stops as soon as
-// a whole digit bucket is taken).  The keys >= T are then compacted.
+// a whole digit bucket is taken, or once the bucket holding T has at most 64 keys, one wavefront picks T from
+// them).  The keys >= T are then compacted.
 //   Chunk   each workgroup reduces 8192 keys of one request to its K best (unordered); repeated until a
 //           request has at most 8192 keys left (one launch for 32 x 512 x 256 -> 512).
 //   Finish  one workgroup selects a request's K keys from at most 8192 (chunk survivors or the scores
