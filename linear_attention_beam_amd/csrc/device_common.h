@@ -37,6 +37,23 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Sum over each group of 8 lanes (the first three steps of row16_sum); every lane of the group receives it.
+__device__ __forceinline__ float row8_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
+  return x;
+}
+
+// Sum over each group of N = 8 or 16 lanes.
+template <int N>
+__device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (N == 16)
+    return row16_sum(x);
+  else
+    return row8_sum(x);
+}
+
 // Sum over a full 64-lane wave; every lane receives it.
 __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);

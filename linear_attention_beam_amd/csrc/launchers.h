@@ -56,14 +56,14 @@ hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Materializing replay (comparison path): dense parent state rebuilt per pair and step.
 hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t s);
 
-// Fused bf16-MFMA step (d_k == 128, d_v % 32 == 0, 32 <= d_v <= 256, L_max <= 64), tiles of 16 or 32 beams.
+// Fused bf16-MFMA step (d_k == 128 or 64, d_v % 32 == 0, 32 <= d_v <= 256, L_max <= 64), tiles of 16 or 32 beams.
 // Steps t >= 2 first run the ancestry-plan kernel, which writes the chain table and per-tile plans into `plan`
 // (fused_plan_bytes).  fused_prepare sets the kernel's LDS limit and returns its persistent grid size.
 bool fused_supported(int d_k, int d_v, int L_max);
-int fused_pick_tile(int d_v, int L_max, int requested);
-size_t fused_lds_bytes(int tile, int L_max, int d_v);
+int fused_pick_tile(int d_k, int d_v, int L_max, int requested);
+size_t fused_lds_bytes(int tile, int L_max, int d_k, int d_v);
 size_t fused_plan_bytes(int R, int B_max, int L_max);
-hipError_t fused_prepare(int tile, int d_v, int L_max, int* grid);
+hipError_t fused_prepare(int tile, int d_k, int d_v, int L_max, int* grid);
 hipError_t launch_step_fused(const StepArgs& a, int tile, void* plan, int grid, hipStream_t s);
 
 // Beam selection: top n_beams of beam_score + logp per request, best first (beam_select.hip).

@@ -199,14 +199,14 @@ onela_status onela_create(const onela_config* cfg, void* d_workspace, size_t wor
   h->tile = 0;
   h->grid = 0;
   if (l.fused) {
-    h->tile = fused_pick_tile(cfg->d_v, cfg->max_steps, cfg->tile_beams);
-    const size_t lds = fused_lds_bytes(h->tile, cfg->max_steps, cfg->d_v);
+    h->tile = fused_pick_tile(cfg->d_k, cfg->d_v, cfg->max_steps, cfg->tile_beams);
+    const size_t lds = fused_lds_bytes(h->tile, cfg->max_steps, cfg->d_k, cfg->d_v);
     if (lds > (size_t)max_lds) {
       delete h;
       return fail(ONELA_ERR_UNSUPPORTED, "tile_beams %d with max_steps %d needs %zu bytes of LDS, the device allows %d",
                   h->tile, cfg->max_steps, lds, max_lds);
     }
-    const hipError_t e = fused_prepare(h->tile, cfg->d_v, cfg->max_steps, &h->grid);
+    const hipError_t e = fused_prepare(h->tile, cfg->d_k, cfg->d_v, cfg->max_steps, &h->grid);
     if (e != hipSuccess) {
       delete h;
       return fail(ONELA_ERR_DEVICE, "fused kernel set-up: %s", hipGetErrorString(e));

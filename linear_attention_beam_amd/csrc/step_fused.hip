@@ -29,8 +29,9 @@
 //     wavefront's 16 rows, so the replay works per beam on 16-byte pieces of u, and u and o leave as float4:
 //       p = A P_k + sum_j c_j (K_j . k) U_j,   u = beta (v - alpha p),
 //       o = alpha (A P_q + sum_j c_j (K_j . q) U_j) + (k . q) u,        A = prod_j alpha_j.
-//   A tile whose distinct records do not fit in LDS reads them from memory instead: 16 lanes per beam take the
-//   key dot products (a different summation order from the matrix cores') and the replay reads u from memory.
+//   A tile whose distinct records do not fit in LDS reads them from memory instead: d_k / 8 lanes per beam take
+//   the key dot products (a different summation order from the matrix cores') and the replay reads u from memory.
+//   The kernel is built for d_k = 128 and d_k = 64 (d_k / 32 matrix-core k-steps, rows of d_k / 8 pieces).
 #include <algorithm>
 
 #include "device_common.h"
@@ -39,9 +40,6 @@
 namespace onela {
 
 namespace {
-constexpr int kDK = 128;        // d_k of the fused kernel
-constexpr int kKS = kDK / 32;   // MFMA k-steps
-constexpr int kRow = 2 * kDK;   // bytes per k or q row (bf16)
 constexpr int kCap = 64;        // distinct ancestor records of a tile staged in LDS (beyond: read from memory)
 constexpr int kSort = 2048;     // beams per request the plan kernel sorts (more: they keep their own order)
 
@@ -49,6 +47,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+// A k or q row of d_k = DK bf16 values is DK / 8 pieces of 16 bytes.  Piece p of row (or record) i of a tile in
+// LDS holds chunk p ^ ONELA_SWZ(i): the 16 rows that one matrix-core operand read touches at one chunk fall in
+// different banks (rows of 256 bytes at d_k = 128, two rows of 128 bytes per 256 at d_k = 64).  A macro, so
+// that the compiler sees the plain mask where it folds the surrounding index arithmetic.
+#define ONELA_SWZ(i) (DK == 128 ? ((i) & 15) : (((i) >> 1) & 7))
 // Bytes per beam of the record places (one per chain position): a multiple of 8, so that the replay reads a
 // beam's places eight at a time.
 __host__ __device__ inline int li_stride(int L) { return (L + 7) & ~7; }
@@ -73,8 +76,9 @@ struct FusedLds {
 // Coefficients per beam: room for the chain rounded up to four positions (those past the chain hold zeros),
 // odd so that 16 beams fall in distinct banks.
 __host__ __device__ inline int coef_stride(int L) { return ((L + 3) & ~3) | 1; }
-__host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB) {
+__host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB, int DK) {
   FusedLds y;
+  const int kRow = 2 * DK;  // bytes per k or q row (bf16)
   int o = 0;
   y.xk = o;  o += NB * kRow;               // k rows, 16-byte pieces swizzled by row
   y.xq = o;  o += NB * kRow;               // q rows
@@ -83,7 +87,7 @@ __host__ __device__ inline FusedLds fused_layout(int NB, int L, int RB) {
   y.be = o;  o += align16(NB * 4);
   y.pm = o;  o += align16(NB * 4);         // the tile's beams
   y.li = o;  o += align16(NB * li_stride(L));  // place of each chain record in the distinct list
-  y.kd = o;  o += kCap * kRow;             // keys of the distinct records
+  y.kd = o;  o += std::max(kCap * kRow, kCap * NB * 8);  // keys of the distinct records, then their dot products
   y.ud = o;  o += kCap * RB * 4;           // their u rows of this row block, 16-byte pieces swizzled by record
   y.ad = o;  o += align16(kCap * 4);       // their alphas at this head
   y.coef = o;   o += NB * coef_stride(L) * 8;
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
 }
 
 // ---------------------------------------------------------------------------------------------------------
-template <int NB, int RB>
+template <int NB, int RB, int DK>
 __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs a, const unsigned char* __restrict__ plan,
                                                                       int plan_bytes, int perm_off, int li_off,
                                                                       Sched S) {
@@ -349,16 +353,20 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
   constexpr int NT = NW * 64;
   constexpr int VP = RB / 8;       // 16-byte pieces of a v row block (bf16)
   constexpr int UP = RB / 4;       // 16-byte pieces of a u row block (float32)
-  constexpr int KI = (kCap * 16 + NT - 1) / NT;  // key pieces of the distinct records per thread
+  constexpr int KP = DK / 8;       // 16-byte pieces of a k or q row (bf16); also lanes per beam below
+  constexpr int KPL = DK == 128 ? 4 : 3;  // log2(KP)
+  constexpr int kKS = DK / 32;     // MFMA k-steps
+  constexpr int kRow = 2 * DK;     // bytes per k or q row
+  constexpr int KI = (kCap * KP + NT - 1) / NT;  // key pieces of the distinct records per thread
   constexpr int UI = (kCap * UP + NT - 1) / NT;  // u pieces per thread
-  constexpr int NX = 2 * NB * 16 + NB * VP;      // k, q and v pieces of a tile
+  constexpr int NX = 2 * NB * KP + NB * VP;      // k, q and v pieces of a tile
   constexpr int XI = (NX + NT - 1) / NT;         // ... per thread
   constexpr int kTiles = NB / 16;
   const int L = a.L_max, H = a.H, n = a.n, d_v = a.d_v, t = a.t, nch = t - 1;
-  const FusedLds lay = fused_layout(NB, L, RB);
+  const FusedLds lay = fused_layout(NB, L, RB, DK);
   const int LS = coef_stride(L), LIS = li_stride(L);
-  constexpr int ngroups = NT / 16;
-  const unsigned hk = (unsigned)H * kDK, hv = (unsigned)H * d_v;  // beam strides of the inputs (elements)
+  constexpr int ngroups = NT / KP;
+  const unsigned hk = (unsigned)H * DK, hv = (unsigned)H * d_v;  // beam strides of the inputs (elements)
   unsigned char* xk = lds + lay.xk;
   unsigned char* xq = lds + lay.xq;
   unsigned char* xv = lds + lay.xv;
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     int nd, as, ab, ks[KI], us[UI], xb[XI];
   };
   auto piece_row = [&](int q) {  // the row (place in the tile) of k, q or v piece q
-    return q < 2 * NB * 16 ? ((q & (NB * 16 - 1)) >> 4) : (q - 2 * NB * 16) / VP;
+    return q < 2 * NB * KP ? ((q & (NB * KP - 1)) >> KPL) : (q - 2 * NB * KP) / VP;
   };
   auto load_plan = [&](const Cursor& c, int tid) {
     Plan p;
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     const int* pm = reinterpret_cast<const int*>(rec + perm_off);
     p.nd = *reinterpret_cast<const int*>(rec);
 #pragma unroll
-    for (int i = 0; i < KI; ++i) p.ks[i] = dl[min((i * NT + tid) >> 4, kCap - 1)];
+    for (int i = 0; i < KI; ++i) p.ks[i] = dl[min((i * NT + tid) >> KPL, kCap - 1)];
 #pragma unroll
     for (int i = 0; i < UI; ++i) p.us[i] = dl[min((i * NT + tid) / UP, kCap - 1)];
     p.as = dl[min(tid, kCap - 1)];
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, col = lane & 15;
-    const int g16 = tid >> 4, j16 = tid & 15;
+    const int gb = tid >> KPL, jb = tid & (KP - 1);  // per-beam work: beam group, piece
     const int rh = c.J.rh, r = rh / H, h = rh - r * H, rb = c.J.rb;
     const int b0 = c.tile * NB, nb = min(NB, n - b0);
     const size_t arena = (size_t)rh * a.slots;
@@ -427,13 +435,12 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     const bool fast = nch > 0 && pl.nd <= kCap;
     const int ndl = fast ? pl.nd : 0;  // records copied into LDS
     {
-      const uint16_t* kr = static_cast<const uint16_t*>(a.rec_k) + arena * kDK;
+      const uint16_t* kr = static_cast<const uint16_t*>(a.rec_k) + arena * DK;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        // key piece p of distinct record d holds chunk p ^ (d % 16): the 16 records an MFMA operand read
-        // touches at one chunk sit in different banks
+        // key piece p of distinct record d holds chunk p ^ ONELA_SWZ(d)
         const int q0 = i * NT + wave * 64, q = q0 + lane;
-        if (q < ndl * 16) dma16(kr + (size_t)pl.ks[i] * kDK + (((q & 15) ^ ((q >> 4) & 15)) << 3), kd + q0 * 16);
+        if (q < ndl * KP) dma16(kr + (size_t)pl.ks[i] * DK + (((q & (KP - 1)) ^ ONELA_SWZ(q >> KPL)) << 3), kd + q0 * 16);
       }
 #pragma unroll
       for (int i = 0; i < UI; ++i) {
@@ -450,21 +457,22 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
       }
     }
     // ---- the k, q and v rows; alpha and beta ----
-    const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rrow * kDK;
-    const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rrow * kDK;
+    const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rrow * DK;
+    const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rrow * DK;
     const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rrow * d_v + rb * RB;
     u32x4_t X[XI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-      // pieces 0 .. NB*16-1: k rows, then q rows, then v rows; a row's piece p holds chunk p ^ (row % 16)
+      // pieces 0 .. NB*KP-1: k rows, then q rows, then v rows; a k or q row's piece p holds chunk p ^ ONELA_SWZ(row),
+      // a v row's chunk p ^ (row % VP)
       const int q = min(i * NT + tid, NX - 1);
       const int row = piece_row(q);
       const unsigned beam = (unsigned)pl.xb[i];
-      const unsigned offk = beam * hk + (((q & 15) ^ (row & 15)) << 3);
-      const int qv = max(q - 2 * NB * 16, 0);
+      const unsigned offk = beam * hk + (((q & (KP - 1)) ^ ONELA_SWZ(row)) << 3);
+      const int qv = max(q - 2 * NB * KP, 0);
       const unsigned offv = beam * hv + (((qv % VP) ^ (row & (VP - 1))) << 3);
-      const uint16_t* base = q < NB * 16 ? kin : (q < 2 * NB * 16 ? qin : vin);
-      X[i] = *reinterpret_cast<const u32x4_t*>(base + (q < 2 * NB * 16 ? offk : offv));
+      const uint16_t* base = q < NB * KP ? kin : (q < 2 * NB * KP ? qin : vin);
+      X[i] = *reinterpret_cast<const u32x4_t*>(base + (q < 2 * NB * KP ? offk : offv));
     }
     const float pal = a.alpha[rrow + (size_t)pl.ab * H];
     const float pbe = a.beta[rrow + (size_t)pl.ab * H];
@@ -495,38 +503,39 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's copies into LDS have landed
     __syncthreads();
-    // ---- per beam (16 lanes): k . q, the record key and alpha; chain coefficients when read from memory ----
-    for (int b = g16; b < nb; b += ngroups) {
+    // ---- per beam (KP lanes): k . q, the record key and alpha; chain coefficients when read from memory ----
+    for (int b = gb; b < nb; b += ngroups) {
       const int beam = pm_t[b];
-      const int xo = b * kRow + ((j16 ^ (b & 15)) << 4);
+      const int xo = b * kRow + ((jb ^ ONELA_SWZ(b)) << 4);
       const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(xk + xo);
       const u32x4_t qx = *reinterpret_cast<const u32x4_t*>(xq + xo);
-      const float kq = row16_sum(dot8_bf16(kx, qx));
+      const float kq = rows_sum<KP>(dot8_bf16(kx, qx));
       if (!fast) {  // step 1 (no chain), or a tile whose distinct records were not staged: newest to oldest
         float cdec = 1.f;
         const int32_t* crow = a.chain_out + ((size_t)r * a.B_max + beam) * L;
         for (int m = nch - 1; m >= 0; --m) {
           const int sl = crow[m];
-          const u32x4_t K = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.rec_k) + (arena + sl) * kDK + j16 * 8);
+          const u32x4_t K = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.rec_k) + (arena + sl) * DK + jb * 8);
           const float am = a.rec_alpha[arena + sl];
-          const float dk = row16_sum(dot8_bf16(K, kx));
-          const float dq = row16_sum(dot8_bf16(K, qx));
-          if (j16 == 0) coef[b * LS + m] = (f32x2_t){cdec * dk, cdec * dq};
+          const float dk = rows_sum<KP>(dot8_bf16(K, kx));
+          const float dq = rows_sum<KP>(dot8_bf16(K, qx));
+          if (jb == 0) coef[b * LS + m] = (f32x2_t){cdec * dk, cdec * dq};
           cdec *= am;
         }
-        if (j16 == 0) beamA[b] = cdec;
+        if (jb == 0) beamA[b] = cdec;
       }
-      if (j16 == 0) beamKq[b] = kq;
+      if (jb == 0) beamKq[b] = kq;
       if (rb == 0) {  // the new record's key and alpha
         const unsigned own = (unsigned)(nch * a.B_max + beam);
-        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.rec_k) + (arena + own) * kDK + j16 * 8) = kx;
-        if (j16 == 0) a.rec_alpha[arena + own] = al_t[b];
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.rec_k) + (arena + own) * DK + jb * 8) = kx;
+        if (jb == 0) a.rec_alpha[arena + own] = al_t[b];
       }
     }
     if (fast) {
       // Dot products of every staged record key with every beam's k and q on the matrix cores:
       // [K_D . k | K_D . q] = K_D [k | q]^T, 16 records x 16 beams per output tile, 4 k-steps of 32.  In an output
-      // tile lane l holds beam l % 16 and records 4 (l / 16) .. +3.  Wavefront w takes tiles w, w + NW, ...
+      // tile lane l holds beam l % 16 and records 4 (l / 16) .. +3; DK / 32 k-steps of 32.  Wavefront w takes
+      // tiles w, w + NW, ...
       const int nrt = (ndl + 15) >> 4;
       const int ntl = nrt * kTiles * 2;
       constexpr int kMaxT = (kCap / 16) * kTiles * 2 / NW + ((kCap / 16) * kTiles * 2 % NW ? 1 : 0);
@@ -542,8 +551,8 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
 #pragma unroll
           for (int k2 = 0; k2 < kKS; ++k2) {
             const int ch = k2 * 4 + gq;
-            const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kd + d * kRow + ((ch ^ (d & 15)) << 4)));
-            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kRow + ((ch ^ (bb & 15)) << 4)));
+            const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kd + d * kRow + ((ch ^ ONELA_SWZ(d)) << 4)));
+            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + bb * kRow + ((ch ^ ONELA_SWZ(bb)) << 4)));
             dacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, kb, dacc[i], 0, 0, 0);
           }
         }
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
       floatx4_t pk = (floatx4_t){0.f, 0.f, 0.f, 0.f}, pq = (floatx4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k2 = 0; k2 < kKS; ++k2) {
-        const int off = bb * kRow + (((k2 * 4 + gq) ^ (bb & 15)) << 4);
+        const int off = bb * kRow + (((k2 * 4 + gq) ^ ONELA_SWZ(bb)) << 4);
         const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xk + off));
         const bf16x8_t bq = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xq + off));
 #pragma unroll
@@ -690,19 +699,21 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
   }
 }
 
+#undef ONELA_SWZ
+
 // ---------------------------------------------------------------------------------------------------------
 bool fused_supported(int d_k, int d_v, int L_max) {
-  return d_k == kDK && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && L_max <= 64 &&
-         fused_lds_bytes(16, L_max, d_v) <= 160 * 1024;
+  return (d_k == 128 || d_k == 64) && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && L_max <= 64 &&
+         fused_lds_bytes(16, L_max, d_k, d_v) <= 160 * 1024;
 }
 
-size_t fused_lds_bytes(int tile, int L_max, int d_v) {
-  return (size_t)fused_layout(tile, L_max, row_block(d_v)).total;
+size_t fused_lds_bytes(int tile, int L_max, int d_k, int d_v) {
+  return (size_t)fused_layout(tile, L_max, row_block(d_v), d_k).total;
 }
 
-int fused_pick_tile(int d_v, int L_max, int requested) {
+int fused_pick_tile(int d_k, int d_v, int L_max, int requested) {
   if (requested) return requested;
-  return fused_lds_bytes(32, L_max, d_v) <= 80 * 1024 ? 32 : 16;
+  return fused_lds_bytes(32, L_max, d_k, d_v) <= 80 * 1024 ? 32 : 16;
 }
 
 namespace {
@@ -720,26 +731,31 @@ size_t fused_plan_bytes(int R, int B_max, int L_max) {
 
 namespace {
 using FusedKernel = void (*)(StepArgs, const unsigned char*, int, int, int, Sched);
-FusedKernel fused_kernel_for(int tile, int rb) {
-#define ONELA_FUSED_RB(NB)                              \
+FusedKernel fused_kernel_for(int tile, int rb, int d_k) {
+#define ONELA_FUSED_RB(NB, DK)                          \
   switch (rb) {                                         \
-    case 32: return &step_fused_kernel<NB, 32>;         \
-    case 64: return &step_fused_kernel<NB, 64>;         \
-    case 128: return &step_fused_kernel<NB, 128>;       \
+    case 32: return &step_fused_kernel<NB, 32, DK>;     \
+    case 64: return &step_fused_kernel<NB, 64, DK>;     \
+    case 128: return &step_fused_kernel<NB, 128, DK>;   \
     default: return nullptr;                            \
   }
-  if (tile == 16) { ONELA_FUSED_RB(16) }
-  if (tile == 32) { ONELA_FUSED_RB(32) }
+  if (d_k == 128) {
+    if (tile == 16) { ONELA_FUSED_RB(16, 128) }
+    if (tile == 32) { ONELA_FUSED_RB(32, 128) }
+  } else if (d_k == 64) {
+    if (tile == 16) { ONELA_FUSED_RB(16, 64) }
+    if (tile == 32) { ONELA_FUSED_RB(32, 64) }
+  }
 #undef ONELA_FUSED_RB
   return nullptr;
 }
 }  // namespace
 
-hipError_t fused_prepare(int tile, int d_v, int L_max, int* grid) {
+hipError_t fused_prepare(int tile, int d_k, int d_v, int L_max, int* grid) {
   const int rb = row_block(d_v);
-  FusedKernel k = fused_kernel_for(tile, rb);
+  FusedKernel k = fused_kernel_for(tile, rb, d_k);
   if (!k) return hipErrorInvalidValue;
-  const size_t lds = fused_lds_bytes(tile, L_max, d_v);
+  const size_t lds = fused_lds_bytes(tile, L_max, d_k, d_v);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -756,7 +772,7 @@ hipError_t fused_prepare(int tile, int d_v, int L_max, int* grid) {
 
 hipError_t launch_step_fused(const StepArgs& a, int tile, void* plan, int grid, hipStream_t s) {
   const int rb = row_block(a.d_v);
-  FusedKernel k = fused_kernel_for(tile, rb);
+  FusedKernel k = fused_kernel_for(tile, rb, a.d_k);
   if (!k) return hipErrorInvalidValue;
   const PlanLayout pl = plan_layout(tile, a.L_max);
   const int ntile = (a.n + tile - 1) / tile;
@@ -774,7 +790,7 @@ hipError_t launch_step_fused(const StepArgs& a, int tile, void* plan, int grid, 
   }
   const Sched S = make_sched(a.R * a.H, a.d_v / rb, ntile, grid);
   const int g = std::min(grid, S.njobs);
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(64 * (rb / 16)), fused_lds_bytes(tile, a.L_max, a.d_v), s, a, pb,
+  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(64 * (rb / 16)), fused_lds_bytes(tile, a.L_max, a.d_k, a.d_v), s, a, pb,
                      pl.bytes, pl.perm, pl.li, S);
   return hipGetLastError();
 }

@@ -202,13 +202,17 @@ hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t) {
   return launched();
 }
 
-bool fused_supported(int d_k, int d_v, int L_max) { return d_k == 128 && d_v % 32 == 0 && d_v >= 32 && L_max <= 64; }
-int fused_pick_tile(int, int, int requested) { return requested ? requested : 32; }
-size_t fused_lds_bytes(int tile, int L_max, int d_v) { return (size_t)tile * (768 + 9 * L_max) + 64 * 768 + d_v; }
+bool fused_supported(int d_k, int d_v, int L_max) {
+  return (d_k == 128 || d_k == 64) && d_v % 32 == 0 && d_v >= 32 && L_max <= 64;
+}
+int fused_pick_tile(int, int, int, int requested) { return requested ? requested : 32; }
+size_t fused_lds_bytes(int tile, int L_max, int d_k, int d_v) {
+  return (size_t)tile * (6 * d_k + 9 * L_max) + 64 * 6 * d_k + d_v;
+}
 size_t fused_plan_bytes(int R, int B_max, int L_max) {
   return (size_t)R * ((B_max + 15) / 16) * (272 + 64 + 16 * L_max) + (size_t)R * B_max * 4;
 }
-hipError_t fused_prepare(int, int, int, int* grid) {
+hipError_t fused_prepare(int, int, int, int, int* grid) {
   *grid = 512;
   return hipSuccess;
 }

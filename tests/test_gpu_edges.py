@@ -67,6 +67,32 @@ def test_ragged_beams(d_v, tile, generic):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
 
 
+@pytest.mark.parametrize("d_v,tile", [(128, 16), (128, 32), (256, 32), (64, 0), (96, 16), (32, 32)])
+def test_fused_dk64(d_v, tile):
+    """d_k = 64 on the fused kernel (rows of 8 pieces, two matrix-core k-steps): ragged beam counts, every
+    head and record against the oracle."""
+    cfg = inputs.config(2, R=3, H=5, d_k=64, d_v=d_v, B=100, L=len(RAGGED))
+    gu.log(f"fused d_k=64 ragged beams {RAGGED} d_v={d_v} tile={tile}")
+    steps = ragged_steps(inputs.decode_inputs(cfg, seed=7), RAGGED)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile, max_beams=128, max_steps=6)
+    assert run.view["fused"] and run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
+
+
+@pytest.mark.parametrize("tile", [16, 32])
+def test_fused_dk64_long_chains(tile):
+    """d_k = 64, 40 steps of 32 beams: late tiles have more distinct records than LDS holds and take the
+    memory path (8 lanes per beam for the key dot products)."""
+    cfg = inputs.config(1, R=1, H=3, d_k=64, d_v=64, B=32, L=40)
+    gu.log(f"fused d_k=64, 40 steps, tile={tile}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile)
+    assert run.view["fused"] and run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
 @pytest.mark.parametrize("d_v,tile", [(128, 16), (96, 32), (224, 16), (32, 0)])
 def test_odd_record_capacity(d_v, tile):
     """max_beams = 37: the slots of a (request, head) are not a multiple of 16, so the fused kernel's last

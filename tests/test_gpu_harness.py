@@ -77,7 +77,8 @@ def test_stack_small():
 
 
 def test_stack_small_odd_dims():
-    """Head sizes only the generic kernels serve (d_k = 64, d_v = 32); 7 candidates, then 40 beams."""
+    """Small head sizes (d_k = 64, d_v = 32, on the fused kernel's smaller row size); 7 candidates, then 40
+    beams."""
     cfg = harness.StackConfig(R=3, B=40, L=3, layers=3, H=3, d_k=64, d_v=32, D=96, n_cand=7,
                               prefill_tokens=8, seed=2)
     rec = check_stack(cfg)

@@ -27,7 +27,8 @@ def draw_case(i):
     tile = int(rng.choice([0, 16, 32]))
     kernel = str(rng.choice(["fused", "fused", "fused", "generic", "materialize"]))
     small_alpha = bool(rng.random() < 1 / 3)
-    return dict(R=R, H=H, d_v=d_v, L=L, B_max=B_max, beams=beams, tile=tile, kernel=kernel,
+    d_k = int(rng.choice([128, 64]))
+    return dict(R=R, H=H, d_k=d_k, d_v=d_v, L=L, B_max=B_max, beams=beams, tile=tile, kernel=kernel,
                 small_alpha=small_alpha)
 
 
@@ -35,7 +36,7 @@ def draw_case(i):
 def test_random_shape(i):
     c = draw_case(i)
     gu.log(f"random shape {i}: {c}")
-    cfg = inputs.config(2, R=c["R"], H=c["H"], d_v=c["d_v"], B=c["B_max"], L=c["L"])
+    cfg = inputs.config(2, R=c["R"], H=c["H"], d_k=c["d_k"], d_v=c["d_v"], B=c["B_max"], L=c["L"])
     steps = ragged_steps(inputs.decode_inputs(cfg, seed=100 + i), c["beams"])
     if c["small_alpha"]:
         rng = np.random.default_rng([0x5A3F, i])
