@@ -87,7 +87,7 @@ enum {
 typedef struct {
   int32_t num_requests; /* R >= 1 */
   int32_t num_heads;    /* H >= 1 */
-  int32_t d_k;          /* 1..256 (the fused MFMA kernel needs d_k == 128 or 64) */
+  int32_t d_k;          /* 1..256 (the fused MFMA kernel needs d_k of 64, 128 or 256) */
   int32_t d_v;          /* 1..256 (the fused MFMA kernel needs d_v % 32 == 0) */
   int32_t max_beams;    /* B_max >= 1: beams per request and step */
   int32_t max_steps;    /* L_max in 1..64: decode steps per context */

@@ -45,13 +45,17 @@ __device__ __forceinline__ float row8_sum(float x) {
   return x;
 }
 
-// Sum over each group of N = 8 or 16 lanes.
+// Sum over each group of N = 8, 16 or 32 lanes (32: two DPP rows joined by a lane exchange).
 template <int N>
 __device__ __forceinline__ float rows_sum(float x) {
-  if constexpr (N == 16)
+  if constexpr (N == 32) {
+    x = row16_sum(x);
+    return x + __shfl_xor(x, 16, 64);
+  } else if constexpr (N == 16) {
     return row16_sum(x);
-  else
+  } else {
     return row8_sum(x);
+  }
 }
 
 // Sum over a full 64-lane wave; every lane receives it.

@@ -56,7 +56,7 @@ hipError_t launch_step_generic(const StepArgs& a, bool bf16, hipStream_t s);
 // Materializing replay (comparison path): dense parent state rebuilt per pair and step.
 hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t s);
 
-// Fused bf16-MFMA step (d_k == 128 or 64, d_v % 32 == 0, 32 <= d_v <= 256, L_max <= 64), tiles of 16 or 32 beams.
+// Fused bf16-MFMA step (d_k of 64, 128 or 256, d_v % 32 == 0, 32 <= d_v <= 256, L_max <= 64), tiles of 16 or 32 beams.
 // Steps t >= 2 first run the ancestry-plan kernel, which writes the chain table and per-tile plans into `plan`
 // (fused_plan_bytes).  fused_prepare sets the kernel's LDS limit and returns its persistent grid size.
 bool fused_supported(int d_k, int d_v, int L_max);

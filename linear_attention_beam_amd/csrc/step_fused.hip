@@ -31,7 +31,8 @@
 //       o = alpha (A P_q + sum_j c_j (K_j . q) U_j) + (k . q) u,        A = prod_j alpha_j.
 //   A tile whose distinct records do not fit in LDS reads them from memory instead: d_k / 8 lanes per beam take
 //   the key dot products (a different summation order from the matrix cores') and the replay reads u from memory.
-//   The kernel is built for d_k = 128 and d_k = 64 (d_k / 32 matrix-core k-steps, rows of d_k / 8 pieces).
+//   The kernel is built for d_k = 64, 128 and 256 (d_k / 32 matrix-core k-steps, rows of d_k / 8 pieces); at
+//   d_k = 256 the S_ctx rows take 64 registers per wavefront and one workgroup runs per compute unit.
 #include <algorithm>
 
 #include "device_common.h"
@@ -49,9 +50,10 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 // A k or q row of d_k = DK bf16 values is DK / 8 pieces of 16 bytes.  Piece p of row (or record) i of a tile in
 // LDS holds chunk p ^ ONELA_SWZ(i): the 16 rows that one matrix-core operand read touches at one chunk fall in
-// different banks (rows of 256 bytes at d_k = 128, two rows of 128 bytes per 256 at d_k = 64).  A macro, so
-// that the compiler sees the plain mask where it folds the surrounding index arithmetic.
-#define ONELA_SWZ(i) (DK == 128 ? ((i) & 15) : (((i) >> 1) & 7))
+// different banks (rows of 256 or 512 bytes at d_k = 128 or 256: 16 chunks of one 256-byte span; two rows of 128
+// bytes per 256 at d_k = 64).  A macro, so that the compiler sees the plain mask where it folds the surrounding
+// index arithmetic.
+#define ONELA_SWZ(i) (DK >= 128 ? ((i) & 15) : (((i) >> 1) & 7))
 // Bytes per beam of the record places (one per chain position): a multiple of 8, so that the replay reads a
 // beam's places eight at a time.
 __host__ __device__ inline int li_stride(int L) { return (L + 7) & ~7; }
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(1024) void ancestry_plan_kernel(StepArgs a, unsigne
 
 // ---------------------------------------------------------------------------------------------------------
 template <int NB, int RB, int DK>
-__global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs a, const unsigned char* __restrict__ plan,
+__global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_kernel(StepArgs a, const unsigned char* __restrict__ plan,
                                                                       int plan_bytes, int perm_off, int li_off,
                                                                       Sched S) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
   constexpr int VP = RB / 8;       // 16-byte pieces of a v row block (bf16)
   constexpr int UP = RB / 4;       // 16-byte pieces of a u row block (float32)
   constexpr int KP = DK / 8;       // 16-byte pieces of a k or q row (bf16); also lanes per beam below
-  constexpr int KPL = DK == 128 ? 4 : 3;  // log2(KP)
+  constexpr int KPL = DK == 256 ? 5 : (DK == 128 ? 4 : 3);  // log2(KP)
   constexpr int kKS = DK / 32;     // MFMA k-steps
   constexpr int kRow = 2 * DK;     // bytes per k or q row
   constexpr int KI = (kCap * KP + NT - 1) / NT;  // key pieces of the distinct records per thread
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(64 * (RB / 16), 4) void step_fused_kernel(StepArgs 
 
 // ---------------------------------------------------------------------------------------------------------
 bool fused_supported(int d_k, int d_v, int L_max) {
-  return (d_k == 128 || d_k == 64) && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && L_max <= 64 &&
+  return (d_k == 128 || d_k == 64 || d_k == 256) && d_v % 32 == 0 && d_v >= 32 && d_v <= 256 && L_max <= 64 &&
          fused_lds_bytes(16, L_max, d_k, d_v) <= 160 * 1024;
 }
 
@@ -713,7 +715,9 @@ size_t fused_lds_bytes(int tile, int L_max, int d_k, int d_v) {
 
 int fused_pick_tile(int d_k, int d_v, int L_max, int requested) {
   if (requested) return requested;
-  return fused_lds_bytes(32, L_max, d_k, d_v) <= 80 * 1024 ? 32 : 16;
+  // 32-beam tiles where two workgroups still fit per CU, or where 16-beam tiles would not fit two either
+  return fused_lds_bytes(32, L_max, d_k, d_v) <= 80 * 1024 || fused_lds_bytes(16, L_max, d_k, d_v) > 80 * 1024
+             ? 32 : 16;
 }
 
 namespace {
@@ -745,6 +749,9 @@ FusedKernel fused_kernel_for(int tile, int rb, int d_k) {
   } else if (d_k == 64) {
     if (tile == 16) { ONELA_FUSED_RB(16, 64) }
     if (tile == 32) { ONELA_FUSED_RB(32, 64) }
+  } else if (d_k == 256) {
+    if (tile == 16) { ONELA_FUSED_RB(16, 256) }
+    if (tile == 32) { ONELA_FUSED_RB(32, 256) }
   }
 #undef ONELA_FUSED_RB
   return nullptr;

@@ -203,7 +203,7 @@ hipError_t launch_step_materialize(const StepArgs& a, bool bf16, hipStream_t) {
 }
 
 bool fused_supported(int d_k, int d_v, int L_max) {
-  return (d_k == 128 || d_k == 64) && d_v % 32 == 0 && d_v >= 32 && L_max <= 64;
+  return (d_k == 128 || d_k == 64 || d_k == 256) && d_v % 32 == 0 && d_v >= 32 && L_max <= 64;
 }
 int fused_pick_tile(int, int, int, int requested) { return requested ? requested : 32; }
 size_t fused_lds_bytes(int tile, int L_max, int d_k, int d_v) {

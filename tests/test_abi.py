@@ -43,7 +43,7 @@ def expected_bytes(c):
     R, H, dk, dv, B, L = c.num_requests, c.num_heads, c.d_k, c.d_v, c.max_beams, c.max_steps
     s_in = 2 if c.qkv_dtype == onela.ONELA_BF16 else 4
     fused = (c.mode == onela.ONELA_MODE_REPLAY and c.qkv_dtype == onela.ONELA_BF16 and not c.flags
-             and dk in (64, 128) and dv % 32 == 0)
+             and dk in (64, 128, 256) and dv % 32 == 0)
     total = 256 + up(R * H * dk * dv * 4) + up(R * H * dk * dv * 4 if fused else 0) + up(L * R * B * L * 4)
     a16 = lambda x: (x + 15) // 16 * 16  # noqa: E731
     # per (request, tile of 16 or 32 beams) plans: nd and up to 64 distinct slots, the tile's beams, one byte per

@@ -67,12 +67,15 @@ def test_ragged_beams(d_v, tile, generic):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
 
 
-@pytest.mark.parametrize("d_v,tile", [(128, 16), (128, 32), (256, 32), (64, 0), (96, 16), (32, 32)])
-def test_fused_dk64(d_v, tile):
-    """d_k = 64 on the fused kernel (rows of 8 pieces, two matrix-core k-steps): ragged beam counts, every
-    head and record against the oracle."""
-    cfg = inputs.config(2, R=3, H=5, d_k=64, d_v=d_v, B=100, L=len(RAGGED))
-    gu.log(f"fused d_k=64 ragged beams {RAGGED} d_v={d_v} tile={tile}")
+@pytest.mark.parametrize("d_k,d_v,tile", [
+    (64, 128, 16), (64, 128, 32), (64, 256, 32), (64, 64, 0), (64, 96, 16), (64, 32, 32),
+    (256, 128, 0), (256, 256, 16), (256, 64, 32), (256, 32, 0), (256, 160, 32),
+])
+def test_fused_head_sizes(d_k, d_v, tile):
+    """d_k = 64 and 256 on the fused kernel (rows of 8 or 32 pieces, 2 or 8 matrix-core k-steps; one workgroup
+    per compute unit at 256): ragged beam counts, every head and record against the oracle."""
+    cfg = inputs.config(2, R=3, H=5, d_k=d_k, d_v=d_v, B=100, L=len(RAGGED))
+    gu.log(f"fused d_k={d_k} ragged beams {RAGGED} d_v={d_v} tile={tile}")
     steps = ragged_steps(inputs.decode_inputs(cfg, seed=7), RAGGED)
     sctx = short_prefill_sctx(cfg)
     run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile, max_beams=128, max_steps=6)
@@ -80,12 +83,12 @@ def test_fused_dk64(d_v, tile):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, 128, 6):.3g}")
 
 
-@pytest.mark.parametrize("tile", [16, 32])
-def test_fused_dk64_long_chains(tile):
-    """d_k = 64, 40 steps of 32 beams: late tiles have more distinct records than LDS holds and take the
-    memory path (8 lanes per beam for the key dot products)."""
-    cfg = inputs.config(1, R=1, H=3, d_k=64, d_v=64, B=32, L=40)
-    gu.log(f"fused d_k=64, 40 steps, tile={tile}")
+@pytest.mark.parametrize("d_k,tile", [(64, 16), (64, 32), (256, 16), (256, 32)])
+def test_fused_head_sizes_long_chains(d_k, tile):
+    """d_k = 64 and 256, 40 steps of 32 beams: late tiles have more distinct records than LDS holds and take
+    the memory path (d_k / 8 lanes per beam for the key dot products)."""
+    cfg = inputs.config(1, R=1, H=3, d_k=d_k, d_v=64, B=32, L=40)
+    gu.log(f"fused d_k={d_k}, 40 steps, tile={tile}")
     steps = inputs.decode_inputs(cfg)
     sctx = short_prefill_sctx(cfg)
     run = gu.GpuRun(cfg, steps, sctx=sctx, tile_beams=tile)

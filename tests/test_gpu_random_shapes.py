@@ -27,7 +27,7 @@ def draw_case(i):
     tile = int(rng.choice([0, 16, 32]))
     kernel = str(rng.choice(["fused", "fused", "fused", "generic", "materialize"]))
     small_alpha = bool(rng.random() < 1 / 3)
-    d_k = int(rng.choice([128, 64]))
+    d_k = int(rng.choice([128, 64, 256]))
     return dict(R=R, H=H, d_k=d_k, d_v=d_v, L=L, B_max=B_max, beams=beams, tile=tile, kernel=kernel,
                 small_alpha=small_alpha)
 
