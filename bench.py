@@ -353,6 +353,62 @@ def traffic_of(config_index: int):
     return None
 
 
+SWEEP_SIZES = (64, 128, 256)
+
+
+def geometry_sweep(torch, onela, inputs, dev, sizes, steps: int = 10, warmup: int = 2):
+    """Decode time over head geometries d_k x d_v (the pages' operator sweep varies the recurrent geometry; its
+    shapes are not listed): R=16 requests x H=16 heads x 512 beams, 6 steps, Zipf(1.1) parents, alpha ~ U(0.95, 1),
+    S_ctx drawn directly (the step's time does not depend on its values).  Each point: the median of `steps`
+    decodes timed with HIP events, algorithmic bytes from the run's own chain tables, and which kernel ran."""
+    points = []
+    for d_k in sizes:
+        for d_v in sizes:
+            cfg = inputs.config(4, R=16, H=16, d_k=d_k, d_v=d_v, B=512, L=6, prefill_steps=0, sctx_std=0.05,
+                                name=f"R=16 H=16 dk={d_k} dv={d_v} B=512 L=6 bf16 zipf1.1")
+            steps_in = inputs.decode_inputs(cfg)
+            dsteps = [dict(q=upload(torch, dev, s.q), k=upload(torch, dev, s.k), v=upload(torch, dev, s.v),
+                           alpha=upload(torch, dev, s.alpha), beta=upload(torch, dev, s.beta),
+                           parent=upload(torch, dev, s.parent)) for s in steps_in]
+            outs = [torch.empty((cfg.R, cfg.B, cfg.H, cfg.d_v), dtype=torch.float32, device=dev)
+                    for _ in range(cfg.L)]
+            ctx = onela.OneLA(cfg.R, cfg.H, cfg.d_k, cfg.d_v, cfg.B, cfg.L, qkv_dtype=cfg.qkv_dtype, device=dev)
+            ctx.set_context(upload(torch, dev, inputs.direct_sctx(cfg)))
+            stream = torch.cuda.current_stream(dev)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for k in range(warmup + steps):
+                ctx.reset()
+                if k >= warmup:
+                    ev[k - warmup][0].record(stream)
+                for t in range(cfg.L):
+                    ctx.step(**dsteps[t], out=outs[t])
+                if k >= warmup:
+                    ev[k - warmup][1].record(stream)
+            torch.cuda.synchronize()
+            if ctx.status() != onela.ONELA_OK:
+                raise RuntimeError("device flag: parent index out of range")
+            view = ctx.view()
+            nbytes = sum(algorithmic_bytes(cfg, view["chains"].cpu().numpy(), [s.parent for s in steps_in]))
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            points.append({"d_k": d_k, "d_v": d_v, "kernel": "fused" if view["fused"] else "fp32",
+                           "ms_per_decode": ms,
+                           "beam_tokens_per_s": cfg.beam_tokens / (ms * 1e-3),
+                           "algorithmic_bytes_per_decode": nbytes,
+                           "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                           "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+            log(f"[bench] sweep d_k={d_k} d_v={d_v}: {ms:.3f} ms/decode, {points[-1]['frac']:.3f} of peak "
+                f"({points[-1]['kernel']})")
+            del view
+            ctx.close()
+            del ctx, dsteps, outs
+            torch.cuda.empty_cache()
+    return {"workload": "R=16 H=16 B=512 L=6 bf16 zipf1.1, S_ctx drawn directly; d_k x d_v over "
+                        + ", ".join(str(x) for x in sizes),
+            "timing": "HIP events around each decode (the plan and fused launches and the gaps between them); "
+                      "median over the timed decodes",
+            "points": points}
+
+
 def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
     """Decode benchmark of one workload: the context from a GPU prefill of the workload's prompt, W warm-up
     decodes, then K timed decodes with HIP events around every decode and every step on the stream the steps
@@ -516,6 +572,7 @@ def main():
     ap.add_argument("--no-materialize", action="store_true", help="skip the materializing-replay comparison")
     ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer random-weight decode")
     ap.add_argument("--stack-layers", type=int, default=4)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the head-geometry sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the benchmark, run a 1 GiB float32 elementwise copy three times (reads 1 GiB, writes "
                          "1 GiB) so hardware counters of a known-size transfer sit in the same profile")
@@ -629,6 +686,9 @@ def main():
         st = line["stack"]
         log(f"[bench] {args.stack_layers}-layer decode: {st['ms_per_decode']:.3f} ms, "
             f"{st['beam_tokens_per_s']:.4g} beam-tokens/s; decode steps ~{100 * st['step_share_est']:.0f}%")
+
+    if not args.no_sweep:
+        line["geometry_sweep"] = geometry_sweep(torch, onela, inputs, dev, SWEEP_SIZES)
 
     if "cpu_baseline" in rec:
         line["cpu_baseline"] = rec["cpu_baseline"]
