@@ -5,12 +5,12 @@ One bench "step" is one whole decode of the workload: L onela_step calls (ancest
 S_ctx contraction, key and query replay, record append, output: at step 1 one fused kernel, later an
 ancestry-plan kernel and the fused kernel) over R requests x B beams x H heads, after onela_reset.  Inputs
 (all L steps) and the context are resident in HBM before timing starts.  value = beam-tokens per second =
-R * B * L / (median seconds per decode over the timed decodes).
+R * B * L / (median seconds per decode over the timed decodes, HIP events at each decode's two ends).
 
 Prints one JSON line.  Extra objects:
   roofline      one onela_step (its two kernels): algorithmic HBM bytes per step (compulsory traffic, counted
-                from the run's own chain tables) / the step's median time from HIP events on its stream in the
-                timed region
+                from the run's own chain tables) / the step's median time from HIP events around each step on
+                its stream, in a second pass of the timed decodes
   configs       the same measurement (decode time, rate, bytes, fraction, FullState speed-up, CPU oracle) for
                 each workload of the table (default: the four GPU-sized workloads, the headline one included)
   cpu_baseline  the float64 CPU oracle (record-replay form) timed on (request, head) pairs of the same
@@ -26,6 +26,7 @@ Prints one JSON line.  Extra objects:
                 request), timed on its own with HIP events; not part of the decode step above
   prefill       onela_prefill of the workload's prompt (the context the decode starts from), against the dense
                 bf16 MFMA peak for the chunked kernels (d_k = 128), else the fp32 vector-ALU peak
+  geometry_sweep  decode time, bytes and fraction over d_k x d_v in {64, 128, 256}^2 at one workload shape
   stack         a whole beam-search decode through several GDN layers with random weights (projections as
                 library GEMMs, one decode context per layer, the GPU beam selection between steps) at the
                 workload's R, H, B, L and head sizes; context for the step's share of a model's decode
@@ -411,9 +412,10 @@ def geometry_sweep(torch, onela, inputs, dev, sizes, steps: int = 10, warmup: in
 
 def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
     """Decode benchmark of one workload: the context from a GPU prefill of the workload's prompt, W warm-up
-    decodes, then K timed decodes with HIP events around every decode and every step on the stream the steps
-    run on.  Returns the per-config record and, for the headline workload, the objects the rest of the line
-    needs."""
+    decodes, then two timed passes of K decodes on the stream the steps run on: HIP events at each decode's ends
+    only (the decode time and throughput), then HIP events around every step as well (the per-launch times of
+    the roofline; each event pair adds a marker between the steps, about 60 us per decode at cfg 3).  Returns
+    the per-config record and, for the headline workload, the objects the rest of the line needs."""
     cfg = inputs.config(index)
     t0 = time.time()
     steps = inputs.decode_inputs(cfg)
@@ -464,17 +466,26 @@ def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
     per_step_bytes = algorithmic_bytes(cfg, chains, [s.parent for s in steps])
 
     K = args.steps
-    step_events = [[[ev(), ev()] for _ in range(cfg.L)] for _ in range(K)]
+    # pass 1: events at the decode's ends (onela_reset enqueues nothing, so a decode is its L steps)
+    ends = [[ev(), ev()] for _ in range(K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for k in range(K):
-        decode(step_events[k])
+        ends[k][0].record(stream)
+        decode()
+        ends[k][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) / K
-    step_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in step_events])     # [K, L]
-    # a decode spans from its first step's start to its last step's end (onela_reset enqueues nothing)
-    decode_ms = np.array([row[0][0].elapsed_time(row[-1][1]) for row in step_events])
+    decode_ms = np.array([a.elapsed_time(b) for a, b in ends])
     ms = float(np.median(decode_ms))
+    # pass 2: events around every step as well
+    step_events = [[[ev(), ev()] for _ in range(cfg.L)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for k in range(K):
+        decode(step_events[k])
+    torch.cuda.synchronize()
+    step_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in step_events])     # [K, L]
+    decode_ms_step_events = np.array([row[0][0].elapsed_time(row[-1][1]) for row in step_events])
     step_med = np.median(step_ms, axis=0)                                                    # [L]
     # the roofline's time: the median decode's steps (the step of each launch pair, its gaps excluded)
     step_sum = float(np.median(step_ms.sum(axis=1)))
@@ -486,6 +497,7 @@ def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
         "ms_per_step": ms,
         "beam_tokens_per_s": cfg.beam_tokens / (ms * 1e-3),
         "decode_ms_min_max": [float(decode_ms.min()), float(decode_ms.max())],
+        "decode_ms_with_step_events": float(np.median(decode_ms_step_events)),
         "algorithmic_bytes_per_launch": sum(per_step_bytes) / cfg.L,
         "algorithmic_bytes_by_decode_step": per_step_bytes,
         "step_us_by_decode_step": [round(float(x) * 1e3, 2) for x in step_med],
@@ -623,7 +635,9 @@ def main():
                      "algorithmic_bytes_per_launch": rec["algorithmic_bytes_per_launch"],
                      "kernel_avg_us": float(np.mean(rec["step_us_by_decode_step"])),
                      "kernel_us_by_decode_step": rec["step_us_by_decode_step"],
-                     "timing": "HIP events around each onela_step on its stream; median over the timed decodes",
+                     "timing": "HIP events around each onela_step on its stream, in a second pass of the timed "
+                               "decodes; median per decode step (value and ms_per_step: events at each decode's "
+                               "ends only, median over the first pass)",
                      "mfma_frac": rec["mfma_frac"]},
         "context_ms": extra["context_ms"],
         # recurrent state kept per (beam, head) after the last step: a dense fp32 matrix (FullState) against the
