@@ -131,6 +131,19 @@ def test_64_step_chains(generic):
     gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
 
 
+@pytest.mark.parametrize("d_k,d_v", [(256, 256), (64, 64)])
+def test_64_step_chains_head_sizes(d_k, d_v):
+    """64-step chains at the largest and smallest fused head sizes (d_k = d_v = 256 needs about 124 KB of LDS per
+    32-beam tile at L = 64)."""
+    cfg = inputs.config(1, R=1, H=2, d_k=d_k, d_v=d_v, B=16, L=64)
+    gu.log(f"64 steps, d_k={d_k} d_v={d_v}")
+    steps = inputs.decode_inputs(cfg)
+    sctx = short_prefill_sctx(cfg)
+    run = gu.GpuRun(cfg, steps, sctx=sctx)
+    assert run.view["fused"] and run.status == onela.ONELA_OK
+    gu.log(f"  max|o err|={check_all_heads(run, cfg, steps, sctx, cfg.B, cfg.L):.3g}")
+
+
 def test_deterministic():
     cfg = inputs.config(2, R=2, H=4, B=256, L=4)
     steps = inputs.decode_inputs(cfg)
