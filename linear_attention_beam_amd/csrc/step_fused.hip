@@ -20,7 +20,8 @@
 //   reused by every beam of every tile of the job).  Per tile:
 //   * one round trip brings everything into LDS: the beams' k, q and v rows (16-byte loads through registers),
 //     and, copied straight into LDS (global_load_lds), the keys, alphas and u rows of the tile's distinct
-//     ancestor records, the beams and the plan places.  The plan itself was loaded during the previous tile;
+//     ancestor records, the beams and the plan places, all issued at a raised wave priority.  The plan itself
+//     was loaded during the previous tile;
 //   * the dot products of every staged record key with every beam's k and q on the matrix cores (16 records x
 //     16 beams per output tile); then one thread per beam walks its chain newest to oldest, scaling them by the
 //     decay product c_j of the alphas after record j;
@@ -433,6 +434,9 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
     const size_t rrow = (size_t)r * n * H + h;  // input row of beam 0 of this request at this head
     const float* u_rd = a.rec_u + arena * d_v;  // u arena of this (request, head): [slots][d_v]
     const unsigned char* prec = plan + ((size_t)r * S.ntile + c.tile) * plan_bytes;
+    // The tile's global loads go out at a raised wave priority: the other workgroup on the CU is usually
+    // computing, and its waves would otherwise win the issue arbitration and delay the loads (7-8% per decode).
+    __builtin_amdgcn_s_setprio(3);
     // ---- the distinct records' keys, u rows and alphas, the beams and the plan places, copied into LDS ----
     const bool fast = nch > 0 && pl.nd <= kCap;
     const int ndl = fast ? pl.nd : 0;  // records copied into LDS
@@ -492,6 +496,7 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
         for (int hl = 0; hl < 2; ++hl)
           sf[k2][hl] = __builtin_bit_cast(bf16x8_t, fr[hl * half + (((size_t)(x >> 1) * kKS + k2) * 2 + (x & 1)) * 64 + lane]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- into LDS ----
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
