@@ -434,8 +434,9 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
     const size_t rrow = (size_t)r * n * H + h;  // input row of beam 0 of this request at this head
     const float* u_rd = a.rec_u + arena * d_v;  // u arena of this (request, head): [slots][d_v]
     const unsigned char* prec = plan + ((size_t)r * S.ntile + c.tile) * plan_bytes;
-    // The tile's global loads go out at a raised wave priority: the other workgroup on the CU is usually
-    // computing, and its waves would otherwise win the issue arbitration and delay the loads (7-8% per decode).
+    // The tile's global loads, and its copies into LDS up to the barrier, run at a raised wave priority: the
+    // other workgroup on the CU is usually computing, and its waves would otherwise win the issue arbitration
+    // and delay them (7-8% per decode).  The output stores below are raised too.
     __builtin_amdgcn_s_setprio(3);
     // ---- the distinct records' keys, u rows and alphas, the beams and the plan places, copied into LDS ----
     const bool fast = nch > 0 && pl.nd <= kCap;
@@ -496,7 +497,6 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
         for (int hl = 0; hl < 2; ++hl)
           sf[k2][hl] = __builtin_bit_cast(bf16x8_t, fr[hl * half + (((size_t)(x >> 1) * kKS + k2) * 2 + (x & 1)) * 64 + lane]);
     }
-    __builtin_amdgcn_s_setprio(0);
     // ---- into LDS ----
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
@@ -510,6 +510,7 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's copies into LDS have landed
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     // ---- per beam (KP lanes): k . q, the record key and alpha; chain coefficients when read from memory ----
     for (int b = gb; b < nb; b += ngroups) {
       const int beam = pm_t[b];
@@ -698,8 +699,10 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
           o4[e] = al * (A * pq[e] + Q[e]) + kq * uu;
         }
         const unsigned own = (unsigned)(nch * a.B_max + beam);
+        __builtin_amdgcn_s_setprio(2);
         *reinterpret_cast<f32x4_t*>(u_wr + (size_t)own * d_v + dv0) = u4;
         *reinterpret_cast<f32x4_t*>(a.o + (rrow + (size_t)beam * H) * d_v + dv0) = o4;
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     __syncthreads();  // the next tile overwrites the LDS
