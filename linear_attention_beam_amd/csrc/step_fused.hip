@@ -129,7 +129,10 @@ __device__ inline Job job_of(const Sched& s, int j) {
   const int per = s.NRB * s.JPR;
   if ((s.RH & 7) == 0) {
     const int x = j & 7, y = j >> 3;
-    q.rh = (y / per) * 8 + x;
+    // group g = y / per holds (request, head) pairs 8g .. 8g + 7; XCD x takes pair 8g + ((x + g) mod 8), so
+    // that each XCD serves every head residue over the groups: the heads' rows sit at fixed offsets in the
+    // beam-major inputs, and with a fixed residue per XCD two of the eight XCDs were 5% slower
+    q.rh = (y / per) * 8 + ((x + y / per) & 7);
     rem = y - (y / per) * per;
   } else {
     q.rh = j / per;
