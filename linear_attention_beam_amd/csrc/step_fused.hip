@@ -437,9 +437,10 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
     const size_t rrow = (size_t)r * n * H + h;  // input row of beam 0 of this request at this head
     const float* u_rd = a.rec_u + arena * d_v;  // u arena of this (request, head): [slots][d_v]
     const unsigned char* prec = plan + ((size_t)r * S.ntile + c.tile) * plan_bytes;
-    // The tile's global loads, and its copies into LDS up to the barrier, run at a raised wave priority: the
-    // other workgroup on the CU is usually computing, and its waves would otherwise win the issue arbitration
-    // and delay them (7-8% per decode).  The output stores below are raised too.
+    // Wave priorities order the two workgroups of a CU: the tile's global loads and its copies into LDS up to
+    // the barrier run at 3 (the other workgroup is usually computing, and its waves would otherwise win the
+    // issue arbitration and delay them: 7-8% per decode), the output stores at 2, the contraction and replay
+    // at 1 (ahead of the other workgroup's per-beam and chain-coefficient work: 2%), the rest at 0.
     __builtin_amdgcn_s_setprio(3);
     // ---- the distinct records' keys, u rows and alphas, the beams and the plan places, copied into LDS ----
     const bool fast = nch > 0 && pl.nd <= kCap;
@@ -621,6 +622,7 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
         for (int idx = tid; idx < (a.B_max - n) * L; idx += NT) a.chain_out[((size_t)r * a.B_max + n) * L + idx] = -1;
     }
     __syncthreads();  // coefficient table ready
+    __builtin_amdgcn_s_setprio(1);
     // ---- per 16-beam tile: S_ctx contraction, replay, new record u, output ----
     const int dvl = wave * 16 + 4 * gq;  // this lane's rows within the row block: dvl .. dvl + 3
     const int dv0 = rb * RB + dvl;
@@ -705,9 +707,10 @@ __global__ __launch_bounds__(64 * (RB / 16), DK == 256 ? 2 : 4) void step_fused_
         __builtin_amdgcn_s_setprio(2);
         *reinterpret_cast<f32x4_t*>(u_wr + (size_t)own * d_v + dv0) = u4;
         *reinterpret_cast<f32x4_t*>(a.o + (rrow + (size_t)beam * H) * d_v + dv0) = o4;
-        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(1);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the next tile overwrites the LDS
   }
 }
