@@ -10,7 +10,9 @@ R * B * L / (median seconds per decode over the timed decodes, HIP events at eac
 Prints one JSON line.  Extra objects:
   roofline      one onela_step (its two kernels): algorithmic HBM bytes per step (compulsory traffic, counted
                 from the run's own chain tables) / the step's median time from HIP events around each step on
-                its stream, in a second pass of the timed decodes
+                its stream, in a second pass of the timed decodes.  `fused_kernel_only`: the same bytes over the
+                fused kernel's own time (plan kernel and launch gap left out) from the committed rocprofv3
+                trace, when it was taken on the current kernel source
   configs       the same measurement (decode time, rate, bytes, fraction, FullState speed-up, CPU oracle) for
                 each workload of the table (default: the four GPU-sized workloads, the headline one included)
   cpu_baseline  the float64 CPU oracle (record-replay form) timed on (request, head) pairs of the same
@@ -343,15 +345,34 @@ def upload(torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def traffic_of(config_index: int):
-    """HBM bytes per step from the committed counter runs, if they were taken on the current kernel source."""
+def profile_of(config_index: int):
+    """The committed rocprofv3 figures of a workload (HBM bytes per step from the counter runs, kernel times per
+    step from the trace), if they were taken on the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     tr = json.load(open(TRAFFIC_FILE))
     key = f"config{config_index}"
     if tr.get("kernel_hash") == kernel_source_hash() and key in tr.get("configs", {}):
-        return tr["configs"][key]["bytes_per_launch"]
+        return tr["configs"][key]
     return None
+
+
+def traffic_of(config_index: int):
+    prof = profile_of(config_index)
+    return prof["bytes_per_launch"] if prof else None
+
+
+def fused_kernel_roofline(config_index: int, bytes_by_step):
+    """The step's algorithmic bytes over the fused kernel's own rocprof time (plan kernel and launch gap left
+    out), from the committed trace of the current kernel source; None without one."""
+    prof = profile_of(config_index)
+    if not prof or "fused_us" not in prof or len(prof["fused_us"]) != len(bytes_by_step):
+        return None
+    us = prof["fused_us"]
+    achieved = sum(bytes_by_step) / (sum(us) * 1e-6) / 1e9
+    return {"kernel": "step_fused_kernel", "us_by_decode_step": us, "plan_us_by_decode_step": prof.get("plan_us"),
+            "achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
+            "source": "rocprofv3 kernel trace of the default bench (profiles/, same kernel source hash)"}
 
 
 SWEEP_SIZES = (64, 128, 256)
@@ -507,6 +528,8 @@ def measure_config(torch, onela, inputs, dev, index: int, args, headline: bool):
         "mfma_frac": mfma_flops / (step_sum * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "wall_ms_per_decode": wall * 1e3,
     }
+    fk = fused_kernel_roofline(index, per_step_bytes)
+    rec["frac_fused_kernel_only"] = fk["frac"] if fk else None
     log(f"[bench] config{index}: {ms:.4f} ms/decode (median of {K}), {rec['beam_tokens_per_s']:.4g} beam-tokens/s, "
         f"{achieved:.0f} GB/s = {rec['frac']:.3f} of peak; steps {rec['step_us_by_decode_step']} us")
     sctx_host = np.ascontiguousarray(np.swapaxes(view["sctx_t"].cpu().numpy(), -1, -2))
@@ -638,7 +661,8 @@ def main():
                      "timing": "HIP events around each onela_step on its stream, in a second pass of the timed "
                                "decodes; median per decode step (value and ms_per_step: events at each decode's "
                                "ends only, median over the first pass)",
-                     "mfma_frac": rec["mfma_frac"]},
+                     "mfma_frac": rec["mfma_frac"],
+                     "fused_kernel_only": fused_kernel_roofline(args.config, rec["algorithmic_bytes_by_decode_step"])},
         "context_ms": extra["context_ms"],
         # recurrent state kept per (beam, head) after the last step: a dense fp32 matrix (FullState) against the
         # records appended along one chain (one per step: k in the input dtype, u fp32, alpha fp32)
