@@ -8,11 +8,11 @@
 // order-preserving unsigned integer (-0 and +0 map alike), the low word is ~f.  Keys are unique, so the
 // top set and its order are unique too.
 //
-// Selection without sorting everything: a workgroup of 1024 threads holds up to 8192 keys in registers
-// (8 per thread) and an MSB-first radix select finds the smallest key T such that exactly K keys are >= T
-// (8-bit digits from the highest bit where the keys differ, one LDS histogram per pass; it stops as soon as
-// a whole digit bucket is taken, or once the bucket holding T has at most 64 keys, one wavefront picks T from
-// them).  The keys >= T are then compacted.
+// Selection without sorting everything: a workgroup holds up to 8192 keys in registers (1024 threads x 8; the
+// chunk pass takes 512 x 16 when there are at least two chunks per CU) and an MSB-first radix select finds
+// the smallest key T such that exactly K keys are >= T (8-bit digits from the highest bit where the keys
+// differ, one LDS histogram per pass; it stops as soon as a whole digit bucket is taken, or once the bucket
+// holding T has at most 64 keys, one wavefront picks T from them).  The keys >= T are then compacted.
 //   Chunk   each workgroup reduces 8192 keys of one request to its K best (unordered); repeated until a
 //           request has at most 8192 keys left (one launch for 32 x 512 x 256 -> 512).
 //   Finish  one workgroup selects a request's K keys from at most 8192 (chunk survivors or the scores
@@ -35,7 +35,7 @@ extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max
 namespace onela {
 
 namespace {
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;                 // finish workgroup: threads, keys per thread
 constexpr int kPerThread = 8;
 constexpr int kChunk = kThreads * kPerThread;  // keys per workgroup
 constexpr int kMaxBeams = 2048;
@@ -64,9 +64,11 @@ struct alignas(16) SelLds {
   uint64_t sorted[kMaxBeams];
 };
 
-// This thread's keys of positions [base, base + kChunk) of request r, position base + e * 1024 + tid in
-// slot e, padded with 0 past n_in.  Built from the scores (src == nullptr) or read from a key buffer.
-__device__ __forceinline__ void load_keys(uint64_t (&key)[kPerThread], const float* beam_scores,
+// This thread's keys of positions [base, base + T P) of request r, position base + e T + tid in slot e,
+// padded with 0 past n_in (T threads, P keys each).  Built from the scores (src == nullptr) or read from a key
+// buffer.
+template <int T, int P>
+__device__ __forceinline__ void load_keys(uint64_t (&key)[P], const float* beam_scores,
                                           const float* logp, const uint64_t* src, long n_in, int n_prev,
                                           int n_cand, int r, long base) {
   const int tid = threadIdx.x;
@@ -74,8 +76,8 @@ __device__ __forceinline__ void load_keys(uint64_t (&key)[kPerThread], const flo
     const float* bs = beam_scores + (size_t)r * n_prev;
     const float* lp = logp + (size_t)r * n_in;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const long i = base + e * kThreads + tid;
+    for (int e = 0; e < P; ++e) {
+      const long i = base + e * T + tid;
       uint64_t k = 0;
       if (i < n_in) {
         const uint32_t f = (uint32_t)i;
@@ -86,8 +88,8 @@ __device__ __forceinline__ void load_keys(uint64_t (&key)[kPerThread], const flo
   } else {
     const uint64_t* s = src + (size_t)r * n_in;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const long i = base + e * kThreads + tid;
+    for (int e = 0; e < P; ++e) {
+      const long i = base + e * T + tid;
       key[e] = i < n_in ? s[i] : 0ull;
     }
   }
@@ -100,11 +102,12 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, i
 
 // The rank-th largest of the cnt (<= kBucket) keys k with (k & mask) == prefix: they are gathered in LDS, and
 // each lane of one wavefront counts the gathered keys above its own.  Every thread must call it.
-__device__ __forceinline__ uint64_t bucket_pick(const uint64_t (&key)[kPerThread], uint64_t prefix, uint64_t mask,
+template <int P>
+__device__ __forceinline__ uint64_t bucket_pick(const uint64_t (&key)[P], uint64_t prefix, uint64_t mask,
                                                 int cnt, int rank, SelLds& sh) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < P; ++e) {
     const bool in = (key[e] & mask) == prefix;  // the keys the last histogram pass counted in the bucket
     const uint64_t take = __ballot(in);
     if (take) {  // one atomic per wavefront
@@ -131,11 +134,12 @@ __device__ __forceinline__ uint64_t bucket_pick(const uint64_t (&key)[kPerThread
 // largest real key differ: the bits above are common to all of them and would only cost passes that split
 // nothing.  Once the bucket that holds T has at most kBucket keys, T is picked from them directly: at
 // 32 x 512 x 256 candidates every chunk then needs at most two histogram passes (up to seven before).
-__device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerThread], int K, SelLds& sh) {
+template <int T, int P>
+__device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[P], int K, SelLds& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, copy = lane & (kHistCopies - 1);
   unsigned long long lo = ~0ull, hi = 0ull;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < P; ++e) {
     const unsigned long long k = key[e];
     if (k != 0ull) {
       lo = k < lo ? k : lo;
@@ -148,13 +152,13 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerTh
     sh.wmin[wave] = lo;
     sh.wmax[wave] = hi;
   }
-  for (int i = tid; i < kHistCopies * kHistStride; i += kThreads) (&sh.hist[0][0])[i] = 0;
+  for (int i = tid; i < kHistCopies * kHistStride; i += T) (&sh.hist[0][0])[i] = 0;
   if (tid == 0) sh.n_bucket = 0;
   __syncthreads();
   lo = ~0ull;
   hi = 0ull;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < T / 64; ++w) {
     lo = sh.wmin[w] < lo ? sh.wmin[w] : lo;
     hi = sh.wmax[w] > hi ? sh.wmax[w] : hi;
   }
@@ -166,7 +170,7 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerTh
   for (;;) {
     const int w = top >= 7 ? 8 : top + 1, shift = top - w + 1;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
+    for (int e = 0; e < P; ++e)
       if ((key[e] & mask) == prefix) atomicAdd(&sh.hist[copy][(int)((key[e] >> shift) & 0xFFu)], 1);
     __syncthreads();
     if (tid < 64) {
@@ -219,12 +223,13 @@ __device__ __forceinline__ uint64_t radix_threshold(const uint64_t (&key)[kPerTh
 }
 
 // Write this workgroup's keys >= thr (K of them) to out[0 .. K) in arbitrary order (out: global or LDS).
-__device__ __forceinline__ void compact(const uint64_t (&key)[kPerThread], uint64_t thr, uint64_t* out, SelLds& sh) {
+template <int P>
+__device__ __forceinline__ void compact(const uint64_t (&key)[P], uint64_t thr, uint64_t* out, SelLds& sh) {
   if (threadIdx.x == 0) sh.n_out = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < P; ++e) {
     const bool mine = key[e] >= thr;
     const uint64_t take = __ballot(mine);
     if (take) {  // one atomic per wave; lanes take consecutive places in lane order
@@ -240,20 +245,21 @@ __device__ __forceinline__ void compact(const uint64_t (&key)[kPerThread], uint6
 
 // One chunk of request r: its K best keys (unordered; all keys, 0-padded, when the chunk holds at most K)
 // to dst[0 .. K).
+template <int T, int P>
 __device__ __forceinline__ void reduce_chunk(const float* beam_scores, const float* logp, const uint64_t* src, long n_in,
                              int n_prev, int n_cand, int r, int c, int K, uint64_t* dst, SelLds& sh) {
-  uint64_t key[kPerThread];
-  const long base = (long)c * kChunk;
-  load_keys(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, base);
+  uint64_t key[P];
+  const long base = (long)c * (T * P);
+  load_keys<T, P>(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, base);
   if (n_in - base <= K) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int i = e * kThreads + threadIdx.x;
+    for (int e = 0; e < P; ++e) {
+      const int i = e * T + threadIdx.x;
       if (i < K) dst[i] = key[e];
     }
     return;
   }
-  compact(key, radix_threshold(key, K, sh), dst, sh);
+  compact<P>(key, radix_threshold<T, P>(key, K, sh), dst, sh);
 }
 
 // Request r's top K of its n_in (<= kChunk) keys, best first, to parent / token / score.
@@ -261,8 +267,8 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
                                int n_prev, int n_cand, int r, int K, int32_t* parent, int32_t* token,
                                float* score, SelLds& sh) {
   uint64_t key[kPerThread];
-  load_keys(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, 0);
-  compact(key, radix_threshold(key, K, sh), sh.best, sh);
+  load_keys<kThreads, kPerThread>(key, beam_scores, logp, src, n_in, n_prev, n_cand, r, 0);
+  compact<kPerThread>(key, radix_threshold<kThreads, kPerThread>(key, K, sh), sh.best, sh);
   // order: each wave sorts runs of 64 survivors in registers (a bitonic network over the lanes, largest
   // first; slots past K hold key 0, which sorts last); then the rank of a survivor is its place in its own
   // run plus, for every other run, the number of that run's keys above it (a binary search).  Keys are
@@ -345,14 +351,17 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
   }
 }
 
-__global__ __launch_bounds__(kThreads, 8) void select_chunk_kernel(const float* __restrict__ beam_scores,
+// T threads of kChunk / T keys each; two workgroups per CU
+template <int T>
+__global__ __launch_bounds__(T, T / 128) void select_chunk_kernel(const float* __restrict__ beam_scores,
                                                                 const float* __restrict__ logp,
                                                                 const uint64_t* __restrict__ src, long n_in,
                                                                 int n_prev, int n_cand, int nchunk, int K,
                                                                 uint64_t* __restrict__ out) {
   __shared__ SelLds sh;
   const int r = blockIdx.x / nchunk, c = blockIdx.x - r * nchunk;
-  reduce_chunk(beam_scores, logp, src, n_in, n_prev, n_cand, r, c, K, out + ((size_t)r * nchunk + c) * K, sh);
+  reduce_chunk<T, kChunk / T>(beam_scores, logp, src, n_in, n_prev, n_cand, r, c, K, out + ((size_t)r * nchunk + c) * K,
+                              sh);
 }
 
 __global__ __launch_bounds__(kThreads, 8) void select_finish_kernel(const float* __restrict__ beam_scores,
@@ -401,6 +410,27 @@ hipError_t beam_select_static_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+// Compute units of the current device, looked up once per device.
+hipError_t compute_units(int* cus) {
+  static std::mutex mu;
+  static int count[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!count[dev]) {
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    count[dev] = c > 0 ? c : 1;
+  }
+  *cus = count[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R, int n_prev, int n_cand,
                               int n_beams, int32_t* parent, int32_t* token, float* score, void* scratch_buf,
                               hipStream_t s) {
@@ -412,13 +442,26 @@ hipError_t launch_beam_select(const float* beam_scores, const float* logp, int R
     return hipGetLastError();
   }
   const long nchunk0 = (n + kChunk - 1) / kChunk;
+  int cus = 0;
+  {
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+  }
   uint64_t* buf[2] = {static_cast<uint64_t*>(scratch_buf), static_cast<uint64_t*>(scratch_buf) + (size_t)R * nchunk0 * K};
   const uint64_t* in = nullptr;
   int which = 0;
   while (n > kChunk) {
     const int nchunk = (int)((n + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(select_chunk_kernel, dim3((unsigned)((size_t)R * nchunk)), dim3(kThreads), 0, s, beam_scores,
-                       logp, in, n, n_prev, n_cand, nchunk, K, buf[which]);
+    // With two chunks per CU or more, 512-thread workgroups (half the waves to dispatch, cheaper barriers);
+    // with fewer, 1024 threads hide more latency per CU.  At 32 x 512 x 256: 25.7 against 26.8 us per call;
+    // at 16 x 512 x 256 (one chunk per CU) 23.1 against 21.7.
+    const unsigned nwg = (unsigned)((size_t)R * nchunk);
+    if (nwg >= 2u * (unsigned)cus)
+      hipLaunchKernelGGL(select_chunk_kernel<512>, dim3(nwg), dim3(512), 0, s, beam_scores, logp, in, n, n_prev, n_cand,
+                         nchunk, K, buf[which]);
+    else
+      hipLaunchKernelGGL(select_chunk_kernel<1024>, dim3(nwg), dim3(1024), 0, s, beam_scores, logp, in, n, n_prev,
+                         n_cand, nchunk, K, buf[which]);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     in = buf[which];
