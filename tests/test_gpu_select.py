@@ -38,6 +38,10 @@ def assert_same(si, n_beams, got):
     (3, 300, 50, 700, True),    # many exact ties: the flat-index order decides
     (1, 1, 9000, 1, True),
     (2, 8193, 1, 7, False),     # one candidate per beam, just over one chunk
+    # 512 chunks of 8192 in the first pass (512-thread chunk workgroups on a 256-CU GPU), then a second chunk
+    # pass over 128 chunks of survivors (1024-thread workgroups), with ties
+    (8, 1024, 512, 2048, True),
+    (32, 512, 256, 64, False),  # 512-thread chunk workgroups, few survivors
 ])
 def test_select_matches_oracle(R, n_prev, n_cand, n_beams, ties):
     gu.log(f"select R={R} n_prev={n_prev} n_cand={n_cand} n_beams={n_beams} ties={ties}")
