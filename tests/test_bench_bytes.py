@@ -20,3 +20,24 @@ def test_algorithmic_bytes_hand_count():
     # records (slots 0 and 2), read once per head: 2 * 2 * 20
     step2 = step1 + 8 + 80
     assert bench.algorithmic_bytes(cfg, chains, parents) == [step1, step2] == [436, 524]
+
+
+def test_fused_kernel_roofline_uses_only_a_profile_of_this_kernel(tmp_path, monkeypatch):
+    """The fused kernel's own fraction comes from the committed trace only when that trace was taken on the
+    current kernel source: bytes over the summed per-step kernel times, against the 8 TB/s peak."""
+    import json
+    prof = {"kernel_hash": bench.kernel_source_hash(),
+            "configs": {"config3": {"bytes_per_launch": [1.0, 1.0], "fused_us": [100.0, 150.0],
+                                    "plan_us": [0.0, 8.0]}}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(prof))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    r = bench.fused_kernel_roofline(3, [600e6, 900e6])
+    # 1.5 GB over 250 us = 6000 GB/s = 0.75 of 8000 GB/s
+    assert abs(r["achieved"] - 6000.0) < 1e-6 and abs(r["frac"] - 0.75) < 1e-12
+    assert bench.fused_kernel_roofline(4, [1.0, 1.0]) is None           # no record of that workload
+    assert bench.fused_kernel_roofline(3, [1.0, 1.0, 1.0]) is None      # another decode length
+    prof["kernel_hash"] = "0" * 16                                       # taken on other code
+    path.write_text(json.dumps(prof))
+    assert bench.fused_kernel_roofline(3, [600e6, 900e6]) is None
+    assert bench.traffic_of(3) is None
