@@ -41,3 +41,16 @@ def test_fused_kernel_roofline_uses_only_a_profile_of_this_kernel(tmp_path, monk
     path.write_text(json.dumps(prof))
     assert bench.fused_kernel_roofline(3, [600e6, 900e6]) is None
     assert bench.traffic_of(3) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch) exits with a message before any GPU
+    work, with a nonzero status."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
