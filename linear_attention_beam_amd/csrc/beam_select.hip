@@ -95,9 +95,28 @@ __device__ __forceinline__ void load_keys(uint64_t (&key)[P], const float* beam_
   }
 }
 
-__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, int off) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, off, 64), hi = __shfl_xor((uint32_t)(x >> 32), off, 64);
-  return ((unsigned long long)hi << 32) | lo;
+// The value of lane (lane ^ off).  Within a row of 16 lanes (off = 1, 2, 4, 8) by DPP register moves: quad
+// permutations for 1 and 2; for 4 and 8 a row shift each way (row_shl:n gives lane i the value of lane i + n,
+// row_shr:n that of lane i - n), and the lane takes the one that stays in its row.  Across rows (16, 32) by a
+// permute through the LDS crossbar.  off must be a constant after inlining.
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int off, int lane) {
+  const int x = (int)v;
+  if (off == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  if (off == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  if (off == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return (uint32_t)((lane & 4) ? dn : up);
+  }
+  if (off == 8) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x108, 0xF, 0xF, false);  // row_shl:8
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    return (uint32_t)((lane & 8) ? dn : up);
+  }
+  return (uint32_t)__shfl_xor(x, off, 64);
+}
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, int off, int lane) {
+  return ((unsigned long long)xor_lane32((uint32_t)(v >> 32), off, lane) << 32) | xor_lane32((uint32_t)v, off, lane);
 }
 
 // The rank-th largest of the cnt (<= kBucket) keys k with (k & mask) == prefix: they are gathered in LDS, and
@@ -281,7 +300,7 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
     for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
       for (int j = k >> 1; j > 0; j >>= 1) {
-        const uint64_t y = shfl_xor64(x, j);
+        const uint64_t y = xor_lane64(x, j, lane);
         const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
         x = take_max ? (x > y ? x : y) : (x < y ? x : y);
       }
