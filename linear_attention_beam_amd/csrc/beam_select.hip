@@ -53,6 +53,13 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t f) {
   return ((uint64_t)score_order(s) << 32) | (uint64_t)(~f);
 }
 
+// The score a key was made from: score_order is one-to-one on every float but the two zeros, which it maps
+// alike (a zero comes back as +0).
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 // LDS of one selection workgroup: the radix histograms and choices, per-wave extremes, and (finish only) the
 // K survivors and their sorted runs of 64.
 struct alignas(16) SelLds {
@@ -357,16 +364,19 @@ __device__ __forceinline__ void finish_request(const float* beam_scores, const f
     }
   }
   __syncthreads();
-  // the score is recomputed from its inputs (the same float32 addition), so its sign survives
+  // the score comes back from the key; a zero score is recomputed from its inputs (the same float32 addition)
+  // so that its sign survives
   const float* bs = beam_scores + (size_t)r * n_prev;
   const float* lp = logp + (size_t)r * n_prev * n_cand;
   for (int i = threadIdx.x; i < K; i += kThreads) {
-    const uint32_t f = ~(uint32_t)sh.best[i];
+    const uint64_t key = sh.best[i];
+    const uint32_t f = ~(uint32_t)key;
     const uint32_t p = f / (uint32_t)n_cand;
     const size_t o = (size_t)r * K + i;
     parent[o] = (int32_t)p;
     token[o] = (int32_t)(f - p * (uint32_t)n_cand);
-    score[o] = bs[p] + lp[f];
+    const float sc = key_score(key);
+    score[o] = sc == 0.f ? bs[p] + lp[f] : sc;
   }
 }
 

@@ -172,3 +172,20 @@ def test_select_reused_garbage_scratch():
                                 scratch=scratch)
         torch.cuda.synchronize()
         assert_same(si, n_beams, [x.cpu().numpy() for x in got])
+
+
+def test_select_signed_zeros():
+    """Scores of -0 (both addends -0) and +0 (other zero sums) rank alike, by flat index, and each keeps the sign
+    of its float32 addition: the keys map both zeros to one value, so the output recomputes zero scores."""
+    gu.log("select with signed zero scores")
+    bs = np.zeros((2, 24), np.float32)
+    lp = np.full((2, 24, 40), -3.0, np.float32)
+    bs[:, ::2] = -0.0
+    lp[:, :, ::3] = -0.0   # beams with bs = -0 give -0 here, beams with bs = +0 give +0
+    lp[:, :, 1::3] = 0.0   # +0 for every beam
+    lp[1, 5, 7] = 2.0 ** -140  # one subnormal score above the zeros
+    si = inputs.SelectInputs(bs, lp)
+    for n_beams in (100, 600):
+        got = run_select(si, n_beams)
+        assert_same(si, n_beams, got)
+        assert np.any(np.signbit(got[2]) & (got[2] == 0)) and np.any(~np.signbit(got[2]) & (got[2] == 0))
