@@ -82,15 +82,26 @@ __device__ __forceinline__ void load_keys(uint64_t (&key)[P], const float* beam_
   if (src == nullptr) {
     const float* bs = beam_scores + (size_t)r * n_prev;
     const float* lp = logp + (size_t)r * n_in;
+    // slot e's flat index is f0 + e T: its beam f / n_cand is stepped (quotient and remainder of T added, one
+    // carry) rather than divided per slot, so the beam-score loads do not wait on P divisions
+    const uint32_t nc = (uint32_t)n_cand, f0 = (uint32_t)(base + tid);
+    const uint32_t dq = (uint32_t)T / nc, dr = (uint32_t)T - dq * nc;
+    uint32_t q = f0 / nc, rm = f0 - q * nc;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
       const long i = base + e * T + tid;
       uint64_t k = 0;
       if (i < n_in) {
         const uint32_t f = (uint32_t)i;
-        k = make_key(bs[f / (uint32_t)n_cand] + lp[f], f);
+        k = make_key(bs[q] + lp[f], f);
       }
       key[e] = k;
+      q += dq;
+      rm += dr;
+      if (rm >= nc) {
+        rm -= nc;
+        ++q;
+      }
     }
   } else {
     const uint64_t* s = src + (size_t)r * n_in;
